@@ -1,0 +1,77 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the CPU checker.
+
+This module holds no attention arithmetic: it only draws numbers. Everything
+is drawn on the CPU with ``torch.Generator`` in fp32 and rounded to bf16
+(round-to-nearest-even, torch's conversion), so every consumer sees the same
+bits whatever device it later copies them to.
+
+Draw order inside one call: Q, K, V, gate logits. Caches and positions come
+from their own calls with their own seeds. Large caches are drawn in chunks,
+chunk c from a generator seeded with (seed, c), so their cost stays linear and
+their content does not depend on how much memory a chunk may use.
+"""
+from __future__ import annotations
+
+import torch
+
+GATE_STD = 2.0  # gate logits ~ N(0, std 2)
+
+
+def _gen(seed: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed) & 0x7FFF_FFFF_FFFF_FFFF)
+    return g
+
+
+def _normal(gen, shape, std=1.0) -> torch.Tensor:
+    x = torch.randn(shape, generator=gen, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x.to(torch.bfloat16)
+
+
+def prefill_inputs(B, S, Hq, Hkv, D=256, seed=0, q_scale=1.0):
+    """Q [B,S,Hq,D], K/V [B,S,Hkv,D] ~ N(0,1); gate logits [B,S,Hq] ~ N(0, 2^2).
+    q_scale multiplies the standard deviation of Q (peaky-softmax cases)."""
+    g = _gen(seed)
+    q = _normal(g, (B, S, Hq, D), q_scale)
+    k = _normal(g, (B, S, Hkv, D))
+    v = _normal(g, (B, S, Hkv, D))
+    gate = _normal(g, (B, S, Hq), GATE_STD)
+    return {"q": q, "k": k, "v": v, "gate": gate}
+
+
+def decode_inputs(B, Hq, Hkv, D=256, seed=0):
+    """q [B,Hq,D], new k/v [B,Hkv,D] ~ N(0,1); gate logits [B,Hq] ~ N(0, 2^2)."""
+    g = _gen(seed)
+    q = _normal(g, (B, Hq, D))
+    k = _normal(g, (B, Hkv, D))
+    v = _normal(g, (B, Hkv, D))
+    gate = _normal(g, (B, Hq), GATE_STD)
+    return {"q": q, "k": k, "v": v, "gate": gate}
+
+
+def cache_tensor(B, Hkv, cap, D=256, seed=0, fill_tokens=None,
+                 chunk_tokens=1 << 15, out=None):
+    """bf16 cache [B, Hkv, cap, D] ~ N(0,1), drawn chunk by chunk along the
+    token axis. Only the first ``fill_tokens`` slots of every (b, head) are
+    drawn (default: all); the rest are zero. ``out`` may supply the
+    destination tensor (e.g. pinned memory)."""
+    fill = cap if fill_tokens is None else int(fill_tokens)
+    if out is None:
+        out = torch.zeros((B, Hkv, cap, D), dtype=torch.bfloat16)
+    c = 0
+    for b in range(B):
+        for h in range(Hkv):
+            for t0 in range(0, fill, chunk_tokens):
+                t1 = min(fill, t0 + chunk_tokens)
+                g = _gen(seed * 1_000_003 + c)
+                out[b, h, t0:t1] = _normal(g, (t1 - t0, D))
+                c += 1
+    return out
+
+
+def positions_uniform(B, lo, hi, seed=0):
+    """int32 positions uniform in [lo, hi)."""
+    g = _gen(seed)
+    return torch.randint(int(lo), int(hi), (B,), generator=g, dtype=torch.int64).to(torch.int32)
