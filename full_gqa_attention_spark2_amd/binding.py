@@ -1,0 +1,233 @@
+"""ctypes binding of libhattn.so (C ABI in include/hattn.h).
+
+Argument marshalling only: torch tensors supply device pointers and the
+current HIP stream; every step of the computation runs in the library's
+kernels. Loading fails loudly if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhattn.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "hattn.h")
+
+LAYER_SLIDING, LAYER_FULL = 0, 1
+KV_RING, KV_LINEAR = 0, 1
+HEAD_DIM = 256
+
+
+class HattnError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn}: status {status} ({msg})")
+        self.status = status
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [
+        ("layer_type", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("rope_theta", ctypes.c_double),
+        ("rotary_fraction", ctypes.c_double),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+    ]
+
+
+class KvCacheC(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("kind", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("capacity", ctypes.c_int32),
+    ]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SIGS = {
+    "hattn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "hattn_layer_defaults": (ctypes.c_int, [_I, _I, _I, ctypes.POINTER(LayerDesc)]),
+    "hattn_rope_apply": (ctypes.c_int, [_P, _I, _I, _I, _P, ctypes.c_double, ctypes.c_double, _P]),
+    "hattn_prefill_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc), ctypes.POINTER(KvCacheC), _I, _I]),
+    "hattn_prefill": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _I, _I, _P,
+                                     ctypes.POINTER(KvCacheC), _P, _P, ctypes.c_size_t, _P]),
+    "hattn_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc), ctypes.POINTER(KvCacheC), _I]),
+    "hattn_decode": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _I, _P, _I,
+                                    ctypes.POINTER(KvCacheC), _P, _P, ctypes.c_size_t, _P]),
+    "hattn_debug_index_probe": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _I, _I, _I, _I, _P, _P, _P, _P]),
+}
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                               "`python -m full_gqa_attention_spark2_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def header_functions():
+    """Names of the functions include/hattn.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hattn_[a-z_0-9]+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return lib().hattn_status_string(status).decode()
+
+
+def _check(fn, status):
+    if status != 0:
+        raise HattnError(fn, status, status_string(status))
+
+
+def _stream(dev=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t, name, dtype=torch.bfloat16, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def layer_desc(layer_type, num_q_heads=16, num_kv_heads=4, **overrides) -> LayerDesc:
+    """The page's parameters for a layer type ("sliding"/"full" or 0/1),
+    with optional overrides of window / rope_theta / rotary_fraction."""
+    lt = {"sliding": LAYER_SLIDING, "full": LAYER_FULL}.get(layer_type, layer_type)
+    d = LayerDesc()
+    _check("hattn_layer_defaults", lib().hattn_layer_defaults(lt, num_q_heads, num_kv_heads, ctypes.byref(d)))
+    for k, v in overrides.items():
+        setattr(d, k, v)
+    return d
+
+
+class KVCache:
+    """A layer's cache: K and V bf16 [B, Hkv, capacity, 256] on the GPU."""
+
+    def __init__(self, k, v, kind):
+        self.k, self.v = k, v
+        self.kind = {"ring": KV_RING, "linear": KV_LINEAR}.get(kind, kind)
+        _need(k, "cache.k")
+        _need(v, "cache.v", shape=k.shape)
+        if k.dim() != 4 or k.shape[3] != HEAD_DIM:
+            raise ValueError("cache tensors must be [B, Hkv, capacity, 256]")
+
+    @classmethod
+    def empty(cls, B, Hkv, capacity, kind, device="cuda"):
+        k = torch.zeros((B, Hkv, capacity, HEAD_DIM), dtype=torch.bfloat16, device=device)
+        return cls(k, torch.zeros_like(k), kind)
+
+    def c(self) -> KvCacheC:
+        return KvCacheC(self.k.data_ptr(), self.v.data_ptr(), self.kind, self.k.shape[0], self.k.shape[2])
+
+
+def prefill_workspace_size(desc, cache, B, S):
+    cc = cache.c()
+    return int(lib().hattn_prefill_workspace_size(ctypes.byref(desc), ctypes.byref(cc), B, S))
+
+
+def decode_workspace_size(desc, cache, B):
+    cc = cache.c()
+    return int(lib().hattn_decode_workspace_size(ctypes.byref(desc), ctypes.byref(cc), B))
+
+
+def _workspace(nbytes, device, ws):
+    if ws is not None:
+        return ws
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def hattn_rope_apply(x, pos, theta, rotary_fraction):
+    """In place RoPE of x bf16 [n_tok, n_heads, head_dim] at int32 pos [n_tok]."""
+    _need(x, "x")
+    _need(pos, "pos", torch.int32, (x.shape[0],))
+    n_tok, n_heads, head_dim = x.shape
+    _check("hattn_rope_apply", lib().hattn_rope_apply(_ptr(x), n_tok, n_heads, head_dim, _ptr(pos),
+                                                       float(theta), float(rotary_fraction), _stream(x.device)))
+    return x
+
+
+def hattn_prefill(desc, q, k, v, gate, start_pos, cache, out=None, workspace=None):
+    """Prefill of q [B,S,Hq,256], k/v [B,S,Hkv,256], gate [B,S,Hq] at host
+    start positions; writes the new keys/values to ``cache``; returns out."""
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    _need(q, "q")
+    _need(k, "k", shape=(B, S, Hkv, D))
+    _need(v, "v", shape=(B, S, Hkv, D))
+    _need(gate, "gate", shape=(B, S, Hq))
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", shape=q.shape)
+    sp = (ctypes.c_int32 * B)(*[int(x) for x in start_pos])
+    cc = cache.c()
+    ws = _workspace(prefill_workspace_size(desc, cache, B, S), q.device, workspace)
+    _check("hattn_prefill", lib().hattn_prefill(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), B, S,
+        ctypes.cast(sp, ctypes.c_void_p), ctypes.byref(cc), _ptr(out), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(q.device)))
+    return out
+
+
+def hattn_decode(desc, q, k, v, gate, pos, max_pos, cache, out=None, workspace=None):
+    """One decode step: q [B,Hq,256], k/v [B,Hkv,256], gate [B,Hq], device
+    int32 positions pos [B] with host bound max_pos; returns out [B,Hq,256]."""
+    B, Hq, D = q.shape
+    Hkv = k.shape[1]
+    _need(q, "q")
+    _need(k, "k", shape=(B, Hkv, D))
+    _need(v, "v", shape=(B, Hkv, D))
+    _need(gate, "gate", shape=(B, Hq))
+    _need(pos, "pos", torch.int32, (B,))
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", shape=q.shape)
+    cc = cache.c()
+    ws = _workspace(decode_workspace_size(desc, cache, B), q.device, workspace)
+    _check("hattn_decode", lib().hattn_decode(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), B, _ptr(pos), int(max_pos),
+        ctypes.byref(cc), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(q.device)))
+    return out
+
+
+def hattn_debug_index_probe(desc, kind, capacity, q_pos0, n_q, device="cuda"):
+    """Device-side mask [n_q, capacity] (uint8), key positions [n_q,
+    capacity] (int32) and own-token slots [n_q] (int32) of a decode view."""
+    kind = {"ring": KV_RING, "linear": KV_LINEAR}.get(kind, kind)
+    mask = torch.empty((n_q, capacity), dtype=torch.uint8, device=device)
+    key_pos = torch.empty((n_q, capacity), dtype=torch.int32, device=device)
+    slot = torch.empty((n_q,), dtype=torch.int32, device=device)
+    _check("hattn_debug_index_probe", lib().hattn_debug_index_probe(
+        ctypes.byref(desc), kind, capacity, q_pos0, n_q, _ptr(mask), _ptr(key_pos), _ptr(slot),
+        _stream(mask.device)))
+    return mask, key_pos, slot

@@ -1,0 +1,383 @@
+// C entry points: argument validation, planning and launches. Every check
+// runs on the host before anything is enqueued.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/hattn.h"
+#include "hattn_internal.h"
+
+using namespace hattn;
+
+namespace {
+
+constexpr int kHeadDimSupported = 256;
+constexpr int kGroupSupported = 4;
+constexpr int kMaxPos = 1 << 30;
+constexpr int kDecodeTargetBlocks = 512;  // ~2 resident blocks per CU
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Rotated channel count, or -1 when head_dim * fraction is not a positive
+// even integer no larger than head_dim.
+int rotary_channels(double fraction, int head_dim) {
+  if (!(fraction > 0.0) || !(fraction <= 1.0)) return -1;
+  const double r = fraction * head_dim;
+  const double ri = floor(r + 0.5);
+  if (fabs(r - ri) > 1e-9 || ri < 2 || ri > head_dim) return -1;
+  const int n = (int)ri;
+  return (n % 2) ? -1 : n;
+}
+
+int check_desc(const hattn_layer_desc* d) {
+  if (!d) return HATTN_ERR_NULL;
+  if (d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->head_dim <= 0) return HATTN_ERR_SHAPE;
+  if (d->num_q_heads % d->num_kv_heads) return HATTN_ERR_SHAPE;
+  if (d->head_dim != kHeadDimSupported) return HATTN_ERR_UNSUPPORTED;
+  if (d->num_q_heads / d->num_kv_heads != kGroupSupported) return HATTN_ERR_UNSUPPORTED;
+  if (!(d->rope_theta > 0.0) || !isfinite(d->rope_theta)) return HATTN_ERR_ROPE;
+  if (rotary_channels(d->rotary_fraction, d->head_dim) < 0) return HATTN_ERR_ROPE;
+  if (d->layer_type == HATTN_LAYER_SLIDING) {
+    if (d->window < 1) return HATTN_ERR_WINDOW;
+  } else if (d->layer_type == HATTN_LAYER_FULL) {
+    if (d->window > 0) return HATTN_ERR_WINDOW;
+  } else {
+    return HATTN_ERR_SHAPE;
+  }
+  return HATTN_OK;
+}
+
+int check_cache(const hattn_layer_desc* d, const hattn_kv_cache* c, int batch) {
+  if (!c) return HATTN_ERR_NULL;
+  if (!c->k || !c->v) return HATTN_ERR_NULL;
+  if (!aligned16(c->k) || !aligned16(c->v)) return HATTN_ERR_ALIGN;
+  if (c->batch != batch || c->capacity < 1) return HATTN_ERR_CACHE;
+  if (c->kind == HATTN_KV_RING) {
+    if (d->layer_type != HATTN_LAYER_SLIDING || c->capacity != d->window) return HATTN_ERR_CACHE;
+  } else if (c->kind != HATTN_KV_LINEAR) {
+    return HATTN_ERR_CACHE;
+  }
+  return HATTN_OK;
+}
+
+hattn_status from_hip(hipError_t e) { return e == hipSuccess ? HATTN_OK : HATTN_ERR_LAUNCH; }
+
+struct PrefillLayout {
+  size_t qhat_bytes;
+  size_t stage_bytes;   // per K or V staging buffer (ring caches only)
+  int stage_rows;
+  size_t total;
+};
+
+PrefillLayout prefill_layout(const hattn_layer_desc* d, const hattn_kv_cache* c, int B, int S) {
+  PrefillLayout L{};
+  L.qhat_bytes = align_up((size_t)B * S * d->num_q_heads * d->head_dim * 2, 256);
+  if (c->kind == HATTN_KV_RING) {
+    L.stage_rows = (d->window - 1) + S;
+    L.stage_bytes = align_up((size_t)B * d->num_kv_heads * L.stage_rows * d->head_dim * 2, 256);
+  }
+  L.total = L.qhat_bytes + 2 * L.stage_bytes;
+  return L;
+}
+
+// Longest visible key range of a decode query at a position <= max_pos.
+long long decode_span(const hattn_layer_desc* d, const hattn_kv_cache* c, long long max_pos) {
+  if (c->kind == HATTN_KV_RING) return std::min<long long>(max_pos + 1, c->capacity);
+  if (d->window > 0) return std::min<long long>(max_pos + 1, d->window);
+  return max_pos + 1;
+}
+
+struct DecodePlan {
+  int nsplit;
+  int split_keys;
+};
+
+// Split the key range so that the grid holds about kDecodeTargetBlocks
+// workgroups, in multiples of 128 keys (one 32-key chunk per wave).
+DecodePlan decode_plan(const hattn_layer_desc* d, const hattn_kv_cache* c, int B, long long span) {
+  const long long base = (long long)B * d->num_kv_heads;
+  long long want = (kDecodeTargetBlocks + base - 1) / base;
+  long long most = (span + 127) / 128;
+  long long n = std::max<long long>(1, std::min(want, most));
+  long long keys = (span + n - 1) / n;
+  keys = (keys + 127) / 128 * 128;
+  n = (span + keys - 1) / keys;
+  DecodePlan p{(int)n, (int)keys};
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hattn_status_string(int status) {
+  switch (status) {
+    case HATTN_OK: return "ok";
+    case HATTN_ERR_NULL: return "null pointer";
+    case HATTN_ERR_SHAPE: return "invalid or inconsistent size";
+    case HATTN_ERR_UNSUPPORTED: return "unsupported head_dim or GQA group size";
+    case HATTN_ERR_ROPE: return "invalid RoPE theta or rotary fraction";
+    case HATTN_ERR_WINDOW: return "window does not match the layer type";
+    case HATTN_ERR_CACHE: return "cache kind, capacity or batch does not fit the layer";
+    case HATTN_ERR_CAPACITY: return "positions exceed the linear cache capacity";
+    case HATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case HATTN_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+    case HATTN_ERR_LAUNCH: return "HIP launch failed";
+    case HATTN_ERR_POSITION: return "position out of range";
+    default: return "unknown status";
+  }
+}
+
+int hattn_layer_defaults(int32_t layer_type, int32_t num_q_heads, int32_t num_kv_heads,
+                         hattn_layer_desc* out) {
+  if (!out) return HATTN_ERR_NULL;
+  hattn_layer_desc d{};
+  d.layer_type = layer_type;
+  d.num_q_heads = num_q_heads;
+  d.num_kv_heads = num_kv_heads;
+  d.head_dim = kHeadDimSupported;
+  if (layer_type == HATTN_LAYER_SLIDING) {
+    d.window = 512;
+    d.rope_theta = 1.0e4;
+    d.rotary_fraction = 1.0;
+  } else if (layer_type == HATTN_LAYER_FULL) {
+    d.window = 0;
+    d.rope_theta = 5.0e6;
+    d.rotary_fraction = 0.25;
+  } else {
+    return HATTN_ERR_SHAPE;
+  }
+  const int st = check_desc(&d);
+  if (st != HATTN_OK) return st;
+  *out = d;
+  return HATTN_OK;
+}
+
+int hattn_rope_apply(void* x, int32_t n_tok, int32_t n_heads, int32_t head_dim, const int32_t* pos,
+                     double theta, double rotary_fraction, hipStream_t stream) {
+  if (n_tok < 0 || n_heads <= 0 || head_dim <= 0 || head_dim % 2) return HATTN_ERR_SHAPE;
+  if (head_dim > 512) return HATTN_ERR_UNSUPPORTED;
+  if (!(theta > 0.0) || !isfinite(theta)) return HATTN_ERR_ROPE;
+  const int r = rotary_channels(rotary_fraction, head_dim);
+  if (r < 0) return HATTN_ERR_ROPE;
+  if (n_tok == 0) return HATTN_OK;
+  if (!x || !pos) return HATTN_ERR_NULL;
+  if (((uintptr_t)x & 1u) || ((uintptr_t)pos & 3u)) return HATTN_ERR_ALIGN;
+  RopeApplyArgs a{};
+  a.x = (uint16_t*)x;
+  a.pos = pos;
+  a.n_tok = n_tok;
+  a.n_heads = n_heads;
+  a.head_dim = head_dim;
+  a.r = r;
+  a.theta = theta;
+  return from_hip(launch_rope_apply(a, stream));
+}
+
+size_t hattn_prefill_workspace_size(const hattn_layer_desc* desc, const hattn_kv_cache* cache,
+                                    int32_t batch, int32_t seq_len) {
+  if (check_desc(desc) != HATTN_OK || !cache || batch <= 0 || seq_len < 0) return 0;
+  return prefill_layout(desc, cache, batch, seq_len).total;
+}
+
+int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
+                  const void* gate, int32_t batch, int32_t seq_len, const int32_t* start_pos,
+                  const hattn_kv_cache* cache, void* out, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+  int st = check_desc(desc);
+  if (st != HATTN_OK) return st;
+  if (batch <= 0 || seq_len < 0) return HATTN_ERR_SHAPE;
+  if (batch > kMaxPrefillBatch) return HATTN_ERR_UNSUPPORTED;
+  st = check_cache(desc, cache, batch);
+  if (st != HATTN_OK) return st;
+  if (!start_pos) return HATTN_ERR_NULL;
+  if (seq_len == 0) return HATTN_OK;
+  if (!q || !k || !v || !gate || !out) return HATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || ((uintptr_t)gate & 1u))
+    return HATTN_ERR_ALIGN;
+  const bool ring = cache->kind == HATTN_KV_RING;
+  for (int b = 0; b < batch; ++b) {
+    const long long s0 = start_pos[b];
+    if (s0 < 0 || s0 + seq_len > kMaxPos) return HATTN_ERR_POSITION;
+    if (!ring && s0 + seq_len > cache->capacity) return HATTN_ERR_CAPACITY;
+  }
+  const PrefillLayout L = prefill_layout(desc, cache, batch, seq_len);
+  if (!workspace || workspace_bytes < L.total) return HATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return HATTN_ERR_ALIGN;
+
+  const int Hq = desc->num_q_heads, Hkv = desc->num_kv_heads;
+  const int r = rotary_channels(desc->rotary_fraction, desc->head_dim);
+  char* ws = (char*)workspace;
+  uint16_t* qhat = (uint16_t*)ws;
+  uint16_t* stage_k = ring ? (uint16_t*)(ws + L.qhat_bytes) : nullptr;
+  uint16_t* stage_v = ring ? (uint16_t*)(ws + L.qhat_bytes + L.stage_bytes) : nullptr;
+  const int w = desc->window;
+
+  // 1. a ring's visible history -> staging rows 0 .. hist-1
+  RingCopyArgs rc{};
+  if (ring) {
+    rc.ring_k = (uint16_t*)cache->k;
+    rc.ring_v = (uint16_t*)cache->v;
+    rc.stage_k = stage_k;
+    rc.stage_v = stage_v;
+    rc.B = batch;
+    rc.Hkv = Hkv;
+    rc.cap = cache->capacity;
+    rc.stage_rows = L.stage_rows;
+    for (int b = 0; b < batch; ++b) {
+      const int hist = std::min(start_pos[b], w - 1);
+      rc.count[b] = hist;
+      rc.first_pos[b] = start_pos[b] - hist;
+      rc.stage_row0[b] = 0;
+    }
+    hipError_t e = launch_ring_to_stage(rc, stream);
+    if (e != hipSuccess) return HATTN_ERR_LAUNCH;
+  }
+
+  // 2. RoPE: Q -> qhat, K/V -> cache slots (linear) or staging rows (ring)
+  PrefillRopeArgs ra{};
+  ra.q = (const uint16_t*)q;
+  ra.k = (const uint16_t*)k;
+  ra.v = (const uint16_t*)v;
+  ra.qhat = qhat;
+  ra.dst_k = ring ? stage_k : (uint16_t*)cache->k;
+  ra.dst_v = ring ? stage_v : (uint16_t*)cache->v;
+  ra.B = batch;
+  ra.S = seq_len;
+  ra.Hq = Hq;
+  ra.Hkv = Hkv;
+  ra.dst_rows = ring ? L.stage_rows : cache->capacity;
+  ra.r = r;
+  ra.theta = desc->rope_theta;
+  PrefillAttnArgs aa{};
+  for (int b = 0; b < batch; ++b) {
+    const int hist = ring ? std::min(start_pos[b], w - 1) : 0;
+    ra.start[b] = start_pos[b];
+    ra.dst_row0[b] = ring ? hist : start_pos[b];
+    aa.start[b] = start_pos[b];
+    aa.key_pos0[b] = ring ? start_pos[b] - hist : 0;
+    aa.n_keys[b] = ring ? hist + seq_len : start_pos[b] + seq_len;
+  }
+  hipError_t e = launch_prefill_rope(ra, stream);
+  if (e != hipSuccess) return HATTN_ERR_LAUNCH;
+
+  // 3. attention over the linear key rows
+  aa.qhat = qhat;
+  aa.kc = ring ? stage_k : (const uint16_t*)cache->k;
+  aa.vc = ring ? stage_v : (const uint16_t*)cache->v;
+  aa.gate = (const uint16_t*)gate;
+  aa.out = (uint16_t*)out;
+  aa.B = batch;
+  aa.S = seq_len;
+  aa.Hq = Hq;
+  aa.Hkv = Hkv;
+  aa.rows = ring ? L.stage_rows : cache->capacity;
+  aa.window = desc->layer_type == HATTN_LAYER_SLIDING ? w : 0;
+  aa.q_tiles = (seq_len + 31) / 32;
+  e = launch_prefill_attn(aa, stream);
+  if (e != hipSuccess) return HATTN_ERR_LAUNCH;
+
+  // 4. a ring keeps the last min(S, capacity) new tokens
+  if (ring) {
+    for (int b = 0; b < batch; ++b) {
+      const int hist = std::min(start_pos[b], w - 1);
+      const int keep = std::min(seq_len, cache->capacity);
+      rc.count[b] = keep;
+      rc.first_pos[b] = start_pos[b] + seq_len - keep;
+      rc.stage_row0[b] = hist + seq_len - keep;
+    }
+    e = launch_stage_to_ring(rc, stream);
+    if (e != hipSuccess) return HATTN_ERR_LAUNCH;
+  }
+  return HATTN_OK;
+}
+
+size_t hattn_decode_workspace_size(const hattn_layer_desc* desc, const hattn_kv_cache* cache,
+                                   int32_t batch) {
+  if (check_desc(desc) != HATTN_OK || !cache || batch <= 0 || cache->capacity < 1) return 0;
+  const long long span = cache->kind == HATTN_KV_RING
+                             ? cache->capacity
+                             : decode_span(desc, cache, (long long)cache->capacity - 1);
+  const DecodePlan p = decode_plan(desc, cache, batch, span);
+  if (p.nsplit == 1) return 256;  // no partials needed; keep a non-zero size
+  const size_t parts = (size_t)batch * desc->num_q_heads * p.nsplit;
+  return align_up(parts * desc->head_dim * 4, 256) + align_up(parts * 2 * 4, 256);
+}
+
+int hattn_decode(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
+                 const void* gate, int32_t batch, const int32_t* pos, int32_t max_pos,
+                 const hattn_kv_cache* cache, void* out, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+  int st = check_desc(desc);
+  if (st != HATTN_OK) return st;
+  if (batch <= 0) return HATTN_ERR_SHAPE;
+  st = check_cache(desc, cache, batch);
+  if (st != HATTN_OK) return st;
+  if (!q || !k || !v || !gate || !pos || !out) return HATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || ((uintptr_t)gate & 1u) ||
+      ((uintptr_t)pos & 3u))
+    return HATTN_ERR_ALIGN;
+  if (max_pos < 0 || max_pos >= kMaxPos) return HATTN_ERR_POSITION;
+  if (cache->kind == HATTN_KV_LINEAR && max_pos >= cache->capacity) return HATTN_ERR_CAPACITY;
+  const long long span = decode_span(desc, cache, max_pos);
+  const DecodePlan p = decode_plan(desc, cache, batch, span);
+  const size_t parts = (size_t)batch * desc->num_q_heads * p.nsplit;
+  const size_t o_bytes = align_up(parts * desc->head_dim * 4, 256);
+  const size_t need = p.nsplit == 1 ? 0 : o_bytes + align_up(parts * 2 * 4, 256);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return HATTN_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return HATTN_ERR_ALIGN;
+
+  DecodeArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.gate = (const uint16_t*)gate;
+  a.pos = pos;
+  a.kc = (uint16_t*)cache->k;
+  a.vc = (uint16_t*)cache->v;
+  a.out = (uint16_t*)out;
+  a.part_o = need ? (float*)workspace : nullptr;
+  a.part_ml = need ? (float*)((char*)workspace + o_bytes) : nullptr;
+  a.B = batch;
+  a.Hq = desc->num_q_heads;
+  a.Hkv = desc->num_kv_heads;
+  a.cap = cache->capacity;
+  a.ring = cache->kind == HATTN_KV_RING;
+  a.window = desc->layer_type == HATTN_LAYER_SLIDING ? desc->window : 0;
+  a.max_pos = max_pos;
+  a.r = rotary_channels(desc->rotary_fraction, desc->head_dim);
+  a.theta = desc->rope_theta;
+  a.nsplit = p.nsplit;
+  a.split_keys = p.split_keys;
+  return from_hip(launch_decode(a, stream));
+}
+
+int hattn_debug_index_probe(const hattn_layer_desc* desc, int32_t kv_kind, int32_t capacity,
+                            int32_t q_pos0, int32_t n_q, uint8_t* mask, int32_t* key_pos,
+                            int32_t* slot, hipStream_t stream) {
+  const int st = check_desc(desc);
+  if (st != HATTN_OK) return st;
+  if (capacity < 1 || n_q < 0) return HATTN_ERR_SHAPE;
+  if (kv_kind != HATTN_KV_RING && kv_kind != HATTN_KV_LINEAR) return HATTN_ERR_CACHE;
+  if (kv_kind == HATTN_KV_RING && (desc->layer_type != HATTN_LAYER_SLIDING || capacity != desc->window))
+    return HATTN_ERR_CACHE;
+  if (q_pos0 < 0 || (long long)q_pos0 + n_q > kMaxPos) return HATTN_ERR_POSITION;
+  if (n_q == 0) return HATTN_OK;
+  if (!mask || !key_pos || !slot) return HATTN_ERR_NULL;
+  ProbeArgs a{};
+  a.mask = mask;
+  a.key_pos = key_pos;
+  a.slot = slot;
+  a.ring = kv_kind == HATTN_KV_RING;
+  a.cap = capacity;
+  a.window = desc->layer_type == HATTN_LAYER_SLIDING ? desc->window : 0;
+  a.q_pos0 = q_pos0;
+  a.n_q = n_q;
+  return from_hip(launch_index_probe(a, stream));
+}
+
+}  // extern "C"

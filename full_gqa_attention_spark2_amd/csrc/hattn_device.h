@@ -1,0 +1,104 @@
+// Device helpers shared by the gfx950 kernels: bf16 rounding, RoPE angles,
+// mask / slot arithmetic, MFMA vector types and LDS swizzles.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hattn {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr int kHeadDim = 256;
+constexpr int kGroup = 4;             // query heads per KV head (both model shapes)
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7fffu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+// fp64 -> bf16 with a single rounding (nearest, ties to even): the value is
+// cut to 8 significant bits in fp64, which is then exact in fp32.
+__device__ __forceinline__ uint16_t double_to_bf16_bits(double x) {
+  if (!(fabs(x) <= 1.7976931348623157e308)) {  // inf or NaN
+    float f = (float)x;
+    return (uint16_t)(__float_as_uint(f) >> 16 | ((x != x) ? 0x40u : 0u));
+  }
+  if (x == 0.0) return (uint16_t)(__float_as_uint((float)x) >> 16);  // keeps sign
+  double r;
+  if (fabs(x) < 0x1p-126) {
+    r = ldexp(rint(ldexp(x, 133)), -133);  // bf16 subnormal spacing 2^-133
+  } else {
+    int e;
+    double m = frexp(x, &e);                // |m| in [0.5, 1)
+    r = ldexp(rint(ldexp(m, 8)), e - 8);
+  }
+  if (fabs(r) > 0x1.fep127) r = copysign(__builtin_inf(), r);
+  return (uint16_t)(__float_as_uint((float)r) >> 16);
+}
+
+// ---------------------------------------------------------------- RoPE
+// Angle of pair i at position p: p * theta^(-2i/r), in fp64.
+__device__ __forceinline__ double rope_angle(int pos, int i, int r, double theta) {
+  double inv_freq = pow(theta, -2.0 * (double)i / (double)r);
+  return (double)pos * inv_freq;
+}
+
+// ---------------------------------------------------------------- masks
+// Visibility of key position pk from query position pq; window <= 0 means
+// unbounded (full causal). Negative pk marks an empty slot.
+__device__ __forceinline__ bool key_visible(int pq, int pk, int window) {
+  return pk >= 0 && pk <= pq && (window <= 0 || pq - pk < window);
+}
+
+// Slot that position p is written to.
+__device__ __forceinline__ int cache_slot(int p, int ring, int cap) {
+  return ring ? (p % cap) : p;
+}
+
+// Position held by `slot` once positions 0..last have been written.
+__device__ __forceinline__ int slot_position(int slot, int last, int ring, int cap) {
+  if (ring) {
+    int d = (last - slot) % cap;
+    if (d < 0) d += cap;
+    int p = last - d;
+    return p >= 0 ? p : -1;
+  }
+  return slot <= last ? slot : -1;
+}
+
+// Contiguous slot range [lo, hi) whose keys a decode query at position p
+// sees (the cache holding positions 0..p).
+__device__ __forceinline__ void decode_key_range(int p, int ring, int cap, int window,
+                                                 int* lo, int* hi) {
+  if (ring) {
+    *lo = 0;
+    *hi = p + 1 < cap ? p + 1 : cap;
+  } else {
+    int l = (window > 0) ? p - window + 1 : 0;
+    *lo = l > 0 ? l : 0;
+    *hi = p + 1;
+  }
+}
+
+// ---------------------------------------------------------------- misc
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_shfl_xor(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+}  // namespace hattn

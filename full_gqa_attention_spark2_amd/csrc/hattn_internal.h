@@ -1,0 +1,98 @@
+// Host-side plans and launch wrappers shared by the C-ABI layer and the
+// kernel translation units. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hattn {
+
+constexpr int kMaxPrefillBatch = 128;
+
+// Token-wise RoPE of the new prefill tokens: rotated Q -> qhat (bf16
+// [B][S][Hq][256]), rotated K and V -> key/value rows of dst (a cache or the
+// staging buffer, [B][Hkv][rows][256]).
+struct PrefillRopeArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* qhat;
+  uint16_t* dst_k;
+  uint16_t* dst_v;
+  int B, S, Hq, Hkv;
+  int dst_rows;     // rows per (b, kv head) in dst
+  int r;            // rotated channels
+  double theta;
+  int start[kMaxPrefillBatch];    // position of token 0 of sequence b
+  int dst_row0[kMaxPrefillBatch]; // dst row of token 0 of sequence b
+};
+
+// Copies between a ring cache and the linear staging buffer.
+struct RingCopyArgs {
+  uint16_t* ring_k;
+  uint16_t* ring_v;
+  uint16_t* stage_k;
+  uint16_t* stage_v;
+  int B, Hkv, cap, stage_rows;
+  int count[kMaxPrefillBatch];     // rows to copy for sequence b
+  int first_pos[kMaxPrefillBatch]; // position of the first copied row
+  int stage_row0[kMaxPrefillBatch];// staging row of the first copied row
+};
+
+struct PrefillAttnArgs {
+  const uint16_t* qhat;   // bf16 [B][S][Hq][256], rotated
+  const uint16_t* kc;     // bf16 [B][Hkv][rows][256], rotated keys
+  const uint16_t* vc;
+  const uint16_t* gate;   // bf16 [B][S][Hq]
+  uint16_t* out;          // bf16 [B][S][Hq][256]
+  int B, S, Hq, Hkv;
+  int rows;               // rows per (b, kv head) in kc / vc
+  int window;             // <= 0: unbounded
+  int q_tiles;            // ceil(S / 32)
+  int start[kMaxPrefillBatch];     // position of query 0
+  int key_pos0[kMaxPrefillBatch];  // position held by key row 0
+  int n_keys[kMaxPrefillBatch];    // valid key rows
+};
+
+struct DecodeArgs {
+  const uint16_t* q;      // bf16 [B][Hq][256]
+  const uint16_t* k;      // bf16 [B][Hkv][256]
+  const uint16_t* v;
+  const uint16_t* gate;   // bf16 [B][Hq]
+  const int* pos;         // int32 [B], device
+  uint16_t* kc;           // cache [B][Hkv][cap][256]
+  uint16_t* vc;
+  uint16_t* out;          // bf16 [B][Hq][256]
+  float* part_o;          // [B][Hq][nsplit][256]
+  float* part_ml;         // [B][Hq][nsplit][2]
+  int B, Hq, Hkv, cap, ring, window, max_pos;
+  int r;
+  double theta;
+  int nsplit;
+  int split_keys;         // keys per split, multiple of 128
+};
+
+struct RopeApplyArgs {
+  uint16_t* x;
+  const int* pos;
+  int n_tok, n_heads, head_dim, r;
+  double theta;
+};
+
+struct ProbeArgs {
+  uint8_t* mask;
+  int* key_pos;
+  int* slot;
+  int ring, cap, window, q_pos0, n_q;
+};
+
+hipError_t launch_prefill_rope(const PrefillRopeArgs& a, hipStream_t s);
+hipError_t launch_ring_to_stage(const RingCopyArgs& a, hipStream_t s);
+hipError_t launch_stage_to_ring(const RingCopyArgs& a, hipStream_t s);
+hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_rope_apply(const RopeApplyArgs& a, hipStream_t s);
+hipError_t launch_index_probe(const ProbeArgs& a, hipStream_t s);
+
+}  // namespace hattn

@@ -7,11 +7,14 @@ bits whatever device it later copies them to.
 
 Draw order inside one call: Q, K, V, gate logits. Caches and positions come
 from their own calls with their own seeds. Large caches are drawn in chunks,
-chunk c from a generator seeded with (seed, c), so their cost stays linear and
-their content does not depend on how much memory a chunk may use.
+chunk c from a PCG64 generator seeded with (seed, c), in parallel threads; the
+content does not depend on the thread count.
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
 import torch
 
 GATE_STD = 2.0  # gate logits ~ N(0, std 2)
@@ -51,23 +54,38 @@ def decode_inputs(B, Hq, Hkv, D=256, seed=0):
     return {"q": q, "k": k, "v": v, "gate": gate}
 
 
+def _cache_chunk(seed, c, n):
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), int(c)])))
+    return torch.from_numpy(rng.standard_normal(n, dtype=np.float32)).to(torch.bfloat16)
+
+
 def cache_tensor(B, Hkv, cap, D=256, seed=0, fill_tokens=None,
-                 chunk_tokens=1 << 15, out=None):
+                 chunk_tokens=1 << 14, out=None, threads=8):
     """bf16 cache [B, Hkv, cap, D] ~ N(0,1), drawn chunk by chunk along the
-    token axis. Only the first ``fill_tokens`` slots of every (b, head) are
-    drawn (default: all); the rest are zero. ``out`` may supply the
-    destination tensor (e.g. pinned memory)."""
+    token axis: chunk c (counting over b, head, token blocks) comes from a
+    PCG64 generator seeded with (seed, c), so chunks can be drawn in
+    parallel and the result does not depend on the thread count. Only the
+    first ``fill_tokens`` slots of every (b, head) are drawn (default: all);
+    the rest are zero. ``out`` may supply the destination (e.g. pinned
+    memory)."""
     fill = cap if fill_tokens is None else int(fill_tokens)
     if out is None:
         out = torch.zeros((B, Hkv, cap, D), dtype=torch.bfloat16)
+    jobs = []
     c = 0
     for b in range(B):
         for h in range(Hkv):
             for t0 in range(0, fill, chunk_tokens):
                 t1 = min(fill, t0 + chunk_tokens)
-                g = _gen(seed * 1_000_003 + c)
-                out[b, h, t0:t1] = _normal(g, (t1 - t0, D))
+                jobs.append((b, h, t0, t1, c))
                 c += 1
+
+    def run(job):
+        b, h, t0, t1, cc = job
+        out[b, h, t0:t1] = _cache_chunk(seed, cc, (t1 - t0) * D).view(t1 - t0, D)
+
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        list(ex.map(run, jobs))
     return out
 
 

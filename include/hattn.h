@@ -1,0 +1,171 @@
+/*
+ * hattn.h - C ABI of the hybrid sliding-window / full causal GQA attention
+ * core for MI355X (gfx950).
+ *
+ * The method (page "Spark-X2.5 架构（4B / 1.7B）"):
+ *   - §2 混合注意力: every layer is either a sliding-window layer (window 512)
+ *     or a full causal layer; three of every four layers slide.
+ *   - §4 分层 RoPE, table: sliding layers rotate all 256 channels with
+ *     theta = 1e4; full layers rotate only the first 64 channels
+ *     (partial_rotary_factor 0.25) with theta = 5e6.
+ *   - §3 逐头输出门控, Eq. 1: out = softmax(Q K^T / sqrt(d_head)) V, multiplied
+ *     by sigmoid of one gate logit per (token, head) in fp32, stored as bf16.
+ *   - §1 config table: 16 query heads share 4 KV heads (8 / 2 for the 1.7B
+ *     shape), head_dim 256, bf16.
+ *   - §6 KV table: full layers keep every token, sliding layers only the last
+ *     512 (page "Spark-X2.5-4B混合注意力架构原理…": the sliding cache keeps the
+ *     512 most recent tokens and drops older ones).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are caller-owned device memory (bf16 unless stated), dense,
+ *     row-major in the layouts given below, 16-byte aligned.
+ *   - The library allocates no device memory and keeps no state beyond
+ *     cached device properties. Every call only enqueues work on `stream`
+ *     (NULL = the default stream); results are valid after the stream
+ *     synchronises.
+ *   - Return value: HATTN_OK (0) or a negative hattn_status; arguments are
+ *     validated on the host before anything is enqueued, so an error return
+ *     leaves device memory untouched. hattn_status_string() names a code.
+ *   - GQA: query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *     Only a group size of 4 and head_dim 256 are supported (both model
+ *     shapes on the page); other values return HATTN_ERR_UNSUPPORTED.
+ *   - Mask: a query at position p_q sees a key at position p_k iff
+ *     p_k <= p_q and, with a window w > 0, p_q - p_k < w (itself plus the
+ *     w - 1 previous tokens).
+ *   - RoPE: r = head_dim * rotary_fraction rotated channels (a positive even
+ *     integer); channel i < r/2 pairs with channel i + r/2 and turns by the
+ *     angle p * theta^(-2i/r), formed in fp64; channels >= r pass through.
+ *     Rotated values are rounded once to bf16 (round to nearest even).
+ *   - Caches store the rotated key and the value as bf16, layout
+ *     [batch][num_kv_heads][capacity][head_dim]. A linear cache keeps
+ *     position p in slot p. A ring cache (sliding layers only) has
+ *     capacity == window and keeps position p in slot p mod capacity.
+ *   - Positions are int32 in [0, 2^30).
+ *   - Calls that touch the same cache must be ordered on one stream.
+ */
+#ifndef HATTN_H
+#define HATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HATTN_OK = 0,
+  HATTN_ERR_NULL = -1,        /* a required pointer is NULL                     */
+  HATTN_ERR_SHAPE = -2,       /* a size is <= 0 or inconsistent                 */
+  HATTN_ERR_UNSUPPORTED = -3, /* head_dim != 256 or group size != 4             */
+  HATTN_ERR_ROPE = -4,        /* theta <= 0 or head_dim*fraction not even int   */
+  HATTN_ERR_WINDOW = -5,      /* sliding layer with window < 1, full with > 0   */
+  HATTN_ERR_CACHE = -6,       /* cache kind/capacity/batch does not fit layer   */
+  HATTN_ERR_CAPACITY = -7,    /* a position does not fit the linear cache       */
+  HATTN_ERR_WORKSPACE = -8,   /* workspace NULL or smaller than required        */
+  HATTN_ERR_ALIGN = -9,       /* a tensor pointer is not 16-byte aligned        */
+  HATTN_ERR_LAUNCH = -10,     /* the HIP runtime refused a launch               */
+  HATTN_ERR_POSITION = -11    /* a host-side position is negative or too large  */
+} hattn_status;
+
+typedef enum { HATTN_LAYER_SLIDING = 0, HATTN_LAYER_FULL = 1 } hattn_layer_type;
+typedef enum { HATTN_KV_RING = 0, HATTN_KV_LINEAR = 1 } hattn_kv_kind;
+
+/* Parameters of one attention layer (page §1 config table, §2, §4 table). */
+typedef struct {
+  int32_t layer_type;      /* hattn_layer_type                                  */
+  int32_t window;          /* sliding: >= 1 (512 on the page); full: <= 0       */
+  double rope_theta;       /* 1e4 sliding, 5e6 full                             */
+  double rotary_fraction;  /* 1.0 sliding, 0.25 full                            */
+  int32_t num_q_heads;     /* 16 (4B) or 8 (1.7B)                               */
+  int32_t num_kv_heads;    /* 4 (4B) or 2 (1.7B)                                */
+  int32_t head_dim;        /* 256                                               */
+} hattn_layer_desc;
+
+/* A caller-owned KV cache of one layer. */
+typedef struct {
+  void* k;           /* bf16 [batch][num_kv_heads][capacity][head_dim]          */
+  void* v;           /* bf16, same layout                                       */
+  int32_t kind;      /* hattn_kv_kind                                           */
+  int32_t batch;     /* number of sequences                                     */
+  int32_t capacity;  /* slots per (sequence, kv head); ring: == window          */
+} hattn_kv_cache;
+
+/* Fill *out with the page's parameters of a layer type (§2, §4 table) for
+ * the given head counts, head_dim 256. */
+int hattn_layer_defaults(int32_t layer_type, int32_t num_q_heads,
+                         int32_t num_kv_heads, hattn_layer_desc* out);
+
+/* RoPE in place (page §4 分层 RoPE, table and text).
+ * x: bf16 [n_tok][n_heads][head_dim], device; pos: int32 [n_tok], device.
+ * Rotates the first head_dim*rotary_fraction channels of every head of
+ * token t by pos[t] as described above; the other channels are untouched. */
+int hattn_rope_apply(void* x, int32_t n_tok, int32_t n_heads, int32_t head_dim,
+                     const int32_t* pos, double theta, double rotary_fraction,
+                     hipStream_t stream);
+
+/* Bytes of device workspace hattn_prefill needs for this call shape. */
+size_t hattn_prefill_workspace_size(const hattn_layer_desc* desc,
+                                    const hattn_kv_cache* cache,
+                                    int32_t batch, int32_t seq_len);
+
+/* Prefill (page §2, §3 Eq. 1, §4): S new tokens per sequence at positions
+ * start_pos[b] + 0 .. S-1, attending to the cache history plus themselves.
+ *   q:    bf16 [B][S][num_q_heads][256]  (before RoPE)
+ *   k, v: bf16 [B][S][num_kv_heads][256] (k before RoPE)
+ *   gate: bf16 [B][S][num_q_heads] gate logits
+ *   start_pos: int32 [B], HOST memory. A linear cache must hold positions
+ *     0 .. start_pos[b]-1 and have capacity >= start_pos[b] + S. A ring
+ *     cache must hold positions up to start_pos[b]-1 as ring slots.
+ *   out:  bf16 [B][S][num_q_heads][256]; must not alias any input.
+ * The rotated keys and the values of the new tokens are written to the cache
+ * (a ring keeps the last min(S, capacity) of them). B <= 128. */
+int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k,
+                  const void* v, const void* gate, int32_t batch,
+                  int32_t seq_len, const int32_t* start_pos,
+                  const hattn_kv_cache* cache, void* out, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace hattn_decode needs for a batch. */
+size_t hattn_decode_workspace_size(const hattn_layer_desc* desc,
+                                   const hattn_kv_cache* cache, int32_t batch);
+
+/* Decode (page §2, §3 Eq. 1, §4; the explainer's per-step cache update): one
+ * new token per sequence at position pos[b].
+ *   q:    bf16 [B][num_q_heads][256], k, v: bf16 [B][num_kv_heads][256]
+ *   gate: bf16 [B][num_q_heads]
+ *   pos:  int32 [B], DEVICE memory; max_pos: a host upper bound of pos[]
+ *     (checked against a linear cache's capacity).
+ *   out:  bf16 [B][num_q_heads][256]
+ * The cache must hold positions 0 .. pos[b]-1. The new rotated key and value
+ * are written to their slot before attention reads the cache. A pos[b]
+ * outside [0, max_pos] yields a NaN output row and no cache write. */
+int hattn_decode(const hattn_layer_desc* desc, const void* q, const void* k,
+                 const void* v, const void* gate, int32_t batch,
+                 const int32_t* pos, int32_t max_pos,
+                 const hattn_kv_cache* cache, void* out, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream);
+
+/* Name of a status code (static string). */
+const char* hattn_status_string(int status);
+
+/* Test hook: the device index helpers the kernels use, evaluated on a grid.
+ * For n_q queries at positions q_pos0 + i and n_keys key slots of a cache
+ * of the given kind/capacity whose next position to write is q_pos0 + i
+ * (decode view), writes
+ *   mask[i][j] (uint8): 1 iff query i sees the key in slot j
+ *   key_pos[i][j] (int32): position held by slot j (-1 if never written)
+ *   slot[i] (int32): slot that query i's own token is written to.
+ * All three outputs are device buffers. */
+int hattn_debug_index_probe(const hattn_layer_desc* desc, int32_t kv_kind,
+                            int32_t capacity, int32_t q_pos0, int32_t n_q,
+                            uint8_t* mask, int32_t* key_pos, int32_t* slot,
+                            hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HATTN_H */

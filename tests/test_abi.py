@@ -1,0 +1,135 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+the header declares, and rejects bad arguments with the documented status
+before touching the device. No kernel is launched here.
+"""
+import ctypes
+import json
+import os
+
+import pytest
+import torch
+
+from full_gqa_attention_spark2_amd import binding as hb
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+# Every call below is built to fail validation; on a machine with a GPU the
+# fake pointers would be dangerous if a check were missing, so these tests
+# only run where no GPU is visible.
+pytestmark = pytest.mark.skipif(torch.cuda.is_available(), reason="host-only ABI checks use fake pointers")
+
+FAKE = 0x10000  # aligned, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def L():
+    return hb.lib()
+
+
+def test_exports_every_header_function(L):
+    names = hb.header_functions()
+    assert {"hattn_rope_apply", "hattn_prefill", "hattn_decode"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in range(0, -12, -1):
+        s = hb.status_string(code)
+        assert s and s != "unknown status"
+    assert hb.status_string(-99) == "unknown status"
+
+
+def test_layer_defaults_match_page_tables():
+    with open(os.path.join(GOLDEN, "spark_layer_config.json")) as f:
+        t = json.load(f)
+    s = hb.layer_desc("sliding", 16, 4)
+    assert (s.window, s.rope_theta, s.rotary_fraction) == (
+        t["models"]["4B"]["sliding_window"], t["rope"]["sliding"]["rope_theta"], t["rope"]["sliding"]["partial_rotary_factor"])
+    f_ = hb.layer_desc("full", 8, 2)
+    assert f_.window <= 0
+    assert (f_.rope_theta, f_.rotary_fraction, f_.head_dim) == (
+        t["rope"]["full"]["rope_theta"], t["rope"]["full"]["partial_rotary_factor"], 256)
+
+
+def _prefill(L, desc, cache, B=1, S=8, start=(0,), ws_bytes=1 << 30, q=FAKE, ws=FAKE, gate=FAKE):
+    sp = (ctypes.c_int32 * len(start))(*start)
+    return L.hattn_prefill(ctypes.byref(desc), q, FAKE, FAKE, gate, B, S, ctypes.cast(sp, ctypes.c_void_p),
+                           ctypes.byref(cache) if cache is not None else None, FAKE, ws, ws_bytes, None)
+
+
+def _decode(L, desc, cache, B=1, max_pos=10, ws_bytes=1 << 30, pos=FAKE):
+    return L.hattn_decode(ctypes.byref(desc), FAKE, FAKE, FAKE, FAKE, B, pos, max_pos,
+                          ctypes.byref(cache), FAKE, FAKE, ws_bytes, None)
+
+
+def test_prefill_rejects_bad_arguments(L):
+    sl = hb.layer_desc("sliding")
+    fu = hb.layer_desc("full")
+    ring = hb.KvCacheC(FAKE, FAKE, hb.KV_RING, 1, 512)
+    lin = hb.KvCacheC(FAKE, FAKE, hb.KV_LINEAR, 1, 64)
+    E = hb
+    cases = []
+    d = hb.layer_desc("sliding"); d.head_dim = 128; cases.append((d, ring, {}, -3))
+    d = hb.layer_desc("sliding"); d.num_q_heads = 8; cases.append((d, ring, {}, -3))      # group 2
+    d = hb.layer_desc("sliding"); d.num_q_heads = 15; cases.append((d, ring, {}, -2))     # not a multiple
+    d = hb.layer_desc("sliding"); d.rotary_fraction = 0.3; cases.append((d, ring, {}, -4))
+    d = hb.layer_desc("sliding"); d.rope_theta = -1.0; cases.append((d, ring, {}, -4))
+    d = hb.layer_desc("sliding"); d.window = 0; cases.append((d, ring, {}, -5))
+    d = hb.layer_desc("full"); d.window = 512; cases.append((d, lin, {}, -5))
+    cases.append((fu, ring, {}, -6))                                                   # ring on a full layer
+    cases.append((sl, hb.KvCacheC(FAKE, FAKE, hb.KV_RING, 1, 256), {}, -6))              # ring cap != window
+    cases.append((sl, hb.KvCacheC(FAKE, FAKE, hb.KV_RING, 2, 512), {}, -6))              # batch mismatch
+    cases.append((sl, hb.KvCacheC(FAKE, FAKE, 7, 1, 512), {}, -6))                       # unknown kind
+    cases.append((fu, lin, {"start": (60,)}, -7))                                      # 60 + 8 > 64
+    cases.append((fu, lin, {"start": (-1,)}, -11))
+    cases.append((fu, lin, {"ws_bytes": 16}, -8))
+    cases.append((fu, lin, {"ws": 0}, -8))
+    cases.append((fu, lin, {"q": FAKE + 2}, -9))
+    cases.append((fu, lin, {"q": 0}, -1))
+    cases.append((fu, hb.KvCacheC(0, FAKE, hb.KV_LINEAR, 1, 64), {}, -1))
+    cases.append((fu, lin, {"B": 0, "start": (0,)}, -2))
+    cases.append((fu, hb.KvCacheC(FAKE, FAKE, hb.KV_LINEAR, 200, 64), {"B": 200, "start": (0,) * 200}, -3))
+    for desc, cache, kw, want in cases:
+        got = _prefill(L, desc, cache, **kw)
+        assert got == want, (desc.layer_type, kw, got, want)
+
+
+def test_decode_rejects_bad_arguments(L):
+    sl = hb.layer_desc("sliding")
+    fu = hb.layer_desc("full")
+    lin = hb.KvCacheC(FAKE, FAKE, hb.KV_LINEAR, 1, 64)
+    assert _decode(L, fu, lin, max_pos=64) == -7       # beyond capacity
+    assert _decode(L, fu, lin, max_pos=-1) == -11
+    assert _decode(L, fu, lin, pos=FAKE + 2) == -9
+    assert _decode(L, fu, lin, pos=0) == -1
+    assert _decode(L, sl, hb.KvCacheC(FAKE, FAKE, hb.KV_RING, 1, 100)) == -6
+    big = hb.KvCacheC(FAKE, FAKE, hb.KV_LINEAR, 1, 1 << 20)
+    assert _decode(L, fu, big, max_pos=(1 << 20) - 1, ws_bytes=100) == -8
+
+
+def test_rope_apply_rejects_bad_arguments(L):
+    f = L.hattn_rope_apply
+    assert f(FAKE, 4, 2, 256, FAKE, 1e4, 0.3, None) == -4
+    assert f(FAKE, 4, 2, 256, FAKE, 0.0, 1.0, None) == -4
+    assert f(FAKE, 4, 2, 1024, FAKE, 1e4, 1.0, None) == -3
+    assert f(FAKE, 4, 2, 255, FAKE, 1e4, 1.0, None) == -2
+    assert f(0, 4, 2, 256, FAKE, 1e4, 1.0, None) == -1
+    assert f(FAKE + 1, 4, 2, 256, FAKE, 1e4, 1.0, None) == -9
+    assert f(0, 0, 2, 256, 0, 1e4, 1.0, None) == 0      # nothing to do
+
+
+def test_workspace_sizes(L):
+    fu = hb.layer_desc("full")
+    sl = hb.layer_desc("sliding")
+    lin = hb.KvCacheC(FAKE, FAKE, hb.KV_LINEAR, 1, 8192)
+    ring = hb.KvCacheC(FAKE, FAKE, hb.KV_RING, 1, 512)
+    # linear prefill: only the rotated Q
+    assert L.hattn_prefill_workspace_size(ctypes.byref(fu), ctypes.byref(lin), 1, 8192) == 8192 * 16 * 256 * 2
+    # ring prefill: rotated Q plus K/V staging of (window - 1 + S) rows
+    got = L.hattn_prefill_workspace_size(ctypes.byref(sl), ctypes.byref(ring), 1, 1024)
+    assert got == 1024 * 16 * 256 * 2 + 2 * 4 * (511 + 1024) * 256 * 2
+    # decode over a 2^20-token linear cache needs split partials
+    big = hb.KvCacheC(FAKE, FAKE, hb.KV_LINEAR, 1, 1 << 20)
+    assert L.hattn_decode_workspace_size(ctypes.byref(fu), ctypes.byref(big), 1) >= 16 * 2 * 256 * 4
+    assert L.hattn_prefill_workspace_size(None, ctypes.byref(lin), 1, 8) == 0
