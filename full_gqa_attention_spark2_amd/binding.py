@@ -63,7 +63,10 @@ _SIGS = {
     "hattn_decode": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _I, _P, _I,
                                     ctypes.POINTER(KvCacheC), _P, _P, ctypes.c_size_t, _P]),
     "hattn_debug_index_probe": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _I, _I, _I, _I, _P, _P, _P, _P]),
+    "hattn_profile_enable": (ctypes.c_int, [ctypes.c_int]),
+    "hattn_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]),
 }
+PROFILE_PREFILL, PROFILE_DECODE = 0, 1
 
 
 def lib():
@@ -231,3 +234,16 @@ def hattn_debug_index_probe(desc, kind, capacity, q_pos0, n_q, device="cuda"):
         ctypes.byref(desc), kind, capacity, q_pos0, n_q, _ptr(mask), _ptr(key_pos), _ptr(slot),
         _stream(mask.device)))
     return mask, key_pos, slot
+
+
+def hattn_profile_enable(enable=True):
+    """Record HIP events around the attention kernels of later calls."""
+    _check("hattn_profile_enable", lib().hattn_profile_enable(1 if enable else 0))
+
+
+def hattn_profile_read(kind):
+    """(count, total_ms) of the recorded kernel sections of one kind."""
+    n = ctypes.c_int64()
+    ms = ctypes.c_double()
+    _check("hattn_profile_read", lib().hattn_profile_read(kind, ctypes.byref(n), ctypes.byref(ms)))
+    return int(n.value), float(ms.value)

@@ -5,8 +5,9 @@
 #include <string.h>
 
 #include <algorithm>
+#include <vector>
 
-#include "../../include/hattn.h"
+#include "hattn.h"
 #include "hattn_internal.h"
 
 using namespace hattn;
@@ -17,6 +18,7 @@ constexpr int kHeadDimSupported = 256;
 constexpr int kGroupSupported = 4;
 constexpr int kMaxPos = 1 << 30;
 constexpr int kDecodeTargetBlocks = 512;  // ~2 resident blocks per CU
+constexpr long long kMaxDecodeSplits = 2048;  // the merge kernel's limit
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -66,6 +68,37 @@ int check_cache(const hattn_layer_desc* d, const hattn_kv_cache* c, int batch) {
 
 hattn_status from_hip(hipError_t e) { return e == hipSuccess ? HATTN_OK : HATTN_ERR_LAUNCH; }
 
+// ---------------------------------------------------------------- profiling
+struct EventPair {
+  hipEvent_t start, stop;
+};
+bool g_profile = false;
+std::vector<EventPair> g_recorded[2];
+std::vector<EventPair> g_free;
+
+// Records the start event of a profiled section; returns the event that
+// closes it (null when profiling is off).
+hipEvent_t profile_begin(int kind, hipStream_t s) {
+  if (!g_profile) return nullptr;
+  EventPair p{};
+  if (!g_free.empty()) {
+    p = g_free.back();
+    g_free.pop_back();
+  } else if (hipEventCreate(&p.start) != hipSuccess || hipEventCreate(&p.stop) != hipSuccess) {
+    return nullptr;
+  }
+  if (hipEventRecord(p.start, s) != hipSuccess) {
+    g_free.push_back(p);
+    return nullptr;
+  }
+  g_recorded[kind].push_back(p);
+  return p.stop;
+}
+
+void profile_end(hipEvent_t stop, hipStream_t s) {
+  if (stop) (void)hipEventRecord(stop, s);
+}
+
 struct PrefillLayout {
   size_t qhat_bytes;
   size_t stage_bytes;   // per K or V staging buffer (ring caches only)
@@ -102,7 +135,7 @@ DecodePlan decode_plan(const hattn_layer_desc* d, const hattn_kv_cache* c, int B
   const long long base = (long long)B * d->num_kv_heads;
   long long want = (kDecodeTargetBlocks + base - 1) / base;
   long long most = (span + 127) / 128;
-  long long n = std::max<long long>(1, std::min(want, most));
+  long long n = std::max<long long>(1, std::min({want, most, (long long)kMaxDecodeSplits}));
   long long keys = (span + n - 1) / n;
   keys = (keys + 127) / 128 * 128;
   n = (span + keys - 1) / keys;
@@ -278,7 +311,9 @@ int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k, co
   aa.rows = ring ? L.stage_rows : cache->capacity;
   aa.window = desc->layer_type == HATTN_LAYER_SLIDING ? w : 0;
   aa.q_tiles = (seq_len + 31) / 32;
+  hipEvent_t prof = profile_begin(HATTN_PROFILE_PREFILL, stream);
   e = launch_prefill_attn(aa, stream);
+  profile_end(prof, stream);
   if (e != hipSuccess) return HATTN_ERR_LAUNCH;
 
   // 4. a ring keeps the last min(S, capacity) new tokens
@@ -353,7 +388,37 @@ int hattn_decode(const hattn_layer_desc* desc, const void* q, const void* k, con
   a.theta = desc->rope_theta;
   a.nsplit = p.nsplit;
   a.split_keys = p.split_keys;
-  return from_hip(launch_decode(a, stream));
+  hipEvent_t prof = profile_begin(HATTN_PROFILE_DECODE, stream);
+  const hipError_t e = launch_decode(a, stream);
+  profile_end(prof, stream);
+  return from_hip(e);
+}
+
+int hattn_profile_enable(int enable) {
+  g_profile = enable != 0;
+  return HATTN_OK;
+}
+
+int hattn_profile_read(int kind, int64_t* count, double* total_ms) {
+  if (kind != HATTN_PROFILE_PREFILL && kind != HATTN_PROFILE_DECODE) return HATTN_ERR_SHAPE;
+  if (!count || !total_ms) return HATTN_ERR_NULL;
+  double sum = 0.0;
+  int64_t n = 0;
+  int st = HATTN_OK;
+  for (EventPair& p : g_recorded[kind]) {
+    float ms = 0.f;
+    if (hipEventSynchronize(p.stop) != hipSuccess || hipEventElapsedTime(&ms, p.start, p.stop) != hipSuccess) {
+      st = HATTN_ERR_LAUNCH;
+    } else {
+      sum += ms;
+      ++n;
+    }
+    g_free.push_back(p);
+  }
+  g_recorded[kind].clear();
+  *count = n;
+  *total_ms = sum;
+  return st;
 }
 
 int hattn_debug_index_probe(const hattn_layer_desc* desc, int32_t kv_kind, int32_t capacity,

@@ -95,11 +95,12 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
       const size_t nk_off = ((size_t)b * a.Hkv + kvh) * kHeadDim;
       a.kc[kv_off + (size_t)slot * kHeadDim + d] = double_to_bf16_bits(rot(a.k + nk_off));
       a.vc[kv_off + (size_t)slot * kHeadDim + d] = a.v[nk_off + d];
-      __threadfence();
     }
   }
+  // Workgroup-scope ordering is enough: the new row is read back only by
+  // this workgroup, through the same CU. (A device-scope fence would write
+  // back and invalidate the whole L2 of the XCD.)
   __syncthreads();
-  __threadfence();
 
   const int col = lane & 15;   // MFMA column / row index of this lane
   const int grp = lane >> 4;   // 16-lane group
@@ -270,28 +271,68 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   }
 }
 
-// Merge of the split partials in split order, gate, bf16 store.
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+// Merge of the split partials, gate, bf16 store. One block per (sequence,
+// head): the block first turns every split's (m, l) into a weight
+// 2^(m_s - M) and the total L, then 4 thread groups each sum a quarter of the
+// splits' partial outputs (8 loads in flight per thread) and combine in a
+// fixed order, so the result does not depend on timing.
+constexpr int kMergeThreads = 1024;
+constexpr int kMaxSplits = 2048;
+
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a) {
+  __shared__ float wgt[kMaxSplits];
+  __shared__ float red[kMergeThreads / 64];
+  __shared__ float part[3][kHeadDim];
   const int b = (int)blockIdx.x / a.Hq;
   const int h = (int)blockIdx.x % a.Hq;
-  const int d = threadIdx.x;
+  const int t = threadIdx.x;
   const int p = a.pos[b];
   uint16_t* o = a.out + ((size_t)b * a.Hq + h) * kHeadDim;
   if (p < 0 || p > a.max_pos) {
-    o[d] = 0x7fc0;
+    if (t < kHeadDim) o[t] = 0x7fc0;
     return;
   }
   const size_t base = ((size_t)b * a.Hq + h) * a.nsplit;
-  float M = -__builtin_inff();
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.part_ml[(base + s) * 2]);
-  float L = 0.f, O = 0.f;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float e = fast_exp2(a.part_ml[(base + s) * 2] - M);
-    L += e * a.part_ml[(base + s) * 2 + 1];
-    O += e * a.part_o[(base + s) * kHeadDim + d];
+  // M = max_s m_s
+  float mx = -__builtin_inff();
+  for (int s = t; s < a.nsplit; s += kMergeThreads) mx = fmaxf(mx, a.part_ml[(base + s) * 2]);
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if ((t & 63) == 0) red[t >> 6] = mx;
+  __syncthreads();
+  float M = red[0];
+  for (int i = 1; i < kMergeThreads / 64; ++i) M = fmaxf(M, red[i]);
+  __syncthreads();
+  // weights and L = sum_s w_s l_s
+  float ls = 0.f;
+  for (int s = t; s < a.nsplit; s += kMergeThreads) {
+    const float w = fast_exp2(a.part_ml[(base + s) * 2] - M);
+    wgt[s] = w;
+    ls += w * a.part_ml[(base + s) * 2 + 1];
   }
-  const float g = bf16_bits_to_float(a.gate[(size_t)b * a.Hq + h]);
-  o[d] = float_to_bf16_bits(O / L * sigmoidf_(g));
+  for (int off = 32; off > 0; off >>= 1) ls += __shfl_xor(ls, off, 64);
+  if ((t & 63) == 0) red[t >> 6] = ls;
+  __syncthreads();
+  float L = 0.f;
+  for (int i = 0; i < kMergeThreads / 64; ++i) L += red[i];
+  // O[d] = sum_s w_s o_s[d]; thread group g takes splits g, g+4, ...
+  const int g = t >> 8, d = t & 255;
+  float acc = 0.f;
+  int s = g;
+  for (; s + 28 < a.nsplit; s += 32) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = a.part_o[(base + s + 4 * u) * kHeadDim + d];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += wgt[s + 4 * u] * v[u];
+  }
+  for (; s < a.nsplit; s += 4) acc += wgt[s] * a.part_o[(base + s) * kHeadDim + d];
+  if (g > 0) part[g - 1][d] = acc;
+  __syncthreads();
+  if (g == 0) {
+    const float O = ((acc + part[0][d]) + part[1][d]) + part[2][d];
+    const float gl = bf16_bits_to_float(a.gate[(size_t)b * a.Hq + h]);
+    o[d] = float_to_bf16_bits(O / L * sigmoidf_(gl));
+  }
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
@@ -300,7 +341,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(decode_kernel, dim3(grid), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(a.B * a.Hq), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(a.B * a.Hq), dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();
 }
 

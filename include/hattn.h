@@ -19,8 +19,8 @@
  * Conventions shared by every entry point
  *   - Tensors are caller-owned device memory (bf16 unless stated), dense,
  *     row-major in the layouts given below, 16-byte aligned.
- *   - The library allocates no device memory and keeps no state beyond
- *     cached device properties. Every call only enqueues work on `stream`
+ *   - The library allocates no device memory and keeps no state beyond the
+ *     profiling events below. Every call only enqueues work on `stream`
  *     (NULL = the default stream); results are valid after the stream
  *     synchronises.
  *   - Return value: HATTN_OK (0) or a negative hattn_status; arguments are
@@ -147,6 +147,16 @@ int hattn_decode(const hattn_layer_desc* desc, const void* q, const void* k,
                  const int32_t* pos, int32_t max_pos,
                  const hattn_kv_cache* cache, void* out, void* workspace,
                  size_t workspace_bytes, hipStream_t stream);
+
+/* Profiling hook for benchmarks. While enabled, every hattn_prefill records
+ * a HIP event pair around its attention kernel (HATTN_PROFILE_PREFILL) and
+ * every hattn_decode around its attention and merge kernels
+ * (HATTN_PROFILE_DECODE), on the call's stream. hattn_profile_read waits for
+ * the recorded events of one kind, returns how many pairs there were and
+ * their summed elapsed milliseconds, and forgets them. Not thread-safe. */
+typedef enum { HATTN_PROFILE_PREFILL = 0, HATTN_PROFILE_DECODE = 1 } hattn_profile_kind;
+int hattn_profile_enable(int enable);
+int hattn_profile_read(int kind, int64_t* count, double* total_ms);
 
 /* Name of a status code (static string). */
 const char* hattn_status_string(int status);
