@@ -42,7 +42,9 @@ int check_desc(const hattn_layer_desc* d) {
   if (d->head_dim != kHeadDimSupported) return HATTN_ERR_UNSUPPORTED;
   if (d->num_q_heads / d->num_kv_heads != kGroupSupported) return HATTN_ERR_UNSUPPORTED;
   if (!(d->rope_theta > 0.0) || !isfinite(d->rope_theta)) return HATTN_ERR_ROPE;
-  if (rotary_channels(d->rotary_fraction, d->head_dim) < 0) return HATTN_ERR_ROPE;
+  const int r = rotary_channels(d->rotary_fraction, d->head_dim);
+  if (r < 0) return HATTN_ERR_ROPE;
+  if (r % 16) return HATTN_ERR_UNSUPPORTED;  // the kernels rotate 8-channel fragments in pairs
   if (d->layer_type == HATTN_LAYER_SLIDING) {
     if (d->window < 1) return HATTN_ERR_WINDOW;
   } else if (d->layer_type == HATTN_LAYER_FULL) {
@@ -67,6 +69,12 @@ int check_cache(const hattn_layer_desc* d, const hattn_kv_cache* c, int batch) {
 }
 
 hattn_status from_hip(hipError_t e) { return e == hipSuccess ? HATTN_OK : HATTN_ERR_LAUNCH; }
+
+// inv_freq_i = theta^(-2i/r), i < r/2, in fp64 (page §4 RoPE table: theta
+// and the rotated-channel count r per layer type).
+void fill_inv_freq(double theta, int r, double* out) {
+  for (int i = 0; i < r / 2; ++i) out[i] = pow(theta, -2.0 * (double)i / (double)r);
+}
 
 // ---------------------------------------------------------------- profiling
 struct EventPair {
@@ -100,7 +108,7 @@ void profile_end(hipEvent_t stop, hipStream_t s) {
 }
 
 struct PrefillLayout {
-  size_t qhat_bytes;
+  size_t table_bytes;   // cos/sin of the new tokens' angles
   size_t stage_bytes;   // per K or V staging buffer (ring caches only)
   int stage_rows;
   size_t total;
@@ -108,12 +116,13 @@ struct PrefillLayout {
 
 PrefillLayout prefill_layout(const hattn_layer_desc* d, const hattn_kv_cache* c, int B, int S) {
   PrefillLayout L{};
-  L.qhat_bytes = align_up((size_t)B * S * d->num_q_heads * d->head_dim * 2, 256);
+  const int r = rotary_channels(d->rotary_fraction, d->head_dim);
+  L.table_bytes = align_up((size_t)B * S * (r / 2) * 8, 256);
   if (c->kind == HATTN_KV_RING) {
     L.stage_rows = (d->window - 1) + S;
     L.stage_bytes = align_up((size_t)B * d->num_kv_heads * L.stage_rows * d->head_dim * 2, 256);
   }
-  L.total = L.qhat_bytes + 2 * L.stage_bytes;
+  L.total = L.table_bytes + 2 * L.stage_bytes;
   return L;
 }
 
@@ -207,7 +216,7 @@ int hattn_rope_apply(void* x, int32_t n_tok, int32_t n_heads, int32_t head_dim, 
   a.n_heads = n_heads;
   a.head_dim = head_dim;
   a.r = r;
-  a.theta = theta;
+  fill_inv_freq(theta, r, a.inv_freq);
   return from_hip(launch_rope_apply(a, stream));
 }
 
@@ -245,9 +254,9 @@ int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k, co
   const int Hq = desc->num_q_heads, Hkv = desc->num_kv_heads;
   const int r = rotary_channels(desc->rotary_fraction, desc->head_dim);
   char* ws = (char*)workspace;
-  uint16_t* qhat = (uint16_t*)ws;
-  uint16_t* stage_k = ring ? (uint16_t*)(ws + L.qhat_bytes) : nullptr;
-  uint16_t* stage_v = ring ? (uint16_t*)(ws + L.qhat_bytes + L.stage_bytes) : nullptr;
+  float2* table = (float2*)ws;
+  uint16_t* stage_k = ring ? (uint16_t*)(ws + L.table_bytes) : nullptr;
+  uint16_t* stage_v = ring ? (uint16_t*)(ws + L.table_bytes + L.stage_bytes) : nullptr;
   const int w = desc->window;
 
   // 1. a ring's visible history -> staging rows 0 .. hist-1
@@ -271,21 +280,20 @@ int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k, co
     if (e != hipSuccess) return HATTN_ERR_LAUNCH;
   }
 
-  // 2. RoPE: Q -> qhat, K/V -> cache slots (linear) or staging rows (ring)
-  PrefillRopeArgs ra{};
-  ra.q = (const uint16_t*)q;
+  // 2. cos/sin table of the new positions; rotated K and V -> cache slots
+  //    (linear) or staging rows (ring)
+  PrefillPrepArgs ra{};
   ra.k = (const uint16_t*)k;
   ra.v = (const uint16_t*)v;
-  ra.qhat = qhat;
+  ra.table = table;
   ra.dst_k = ring ? stage_k : (uint16_t*)cache->k;
   ra.dst_v = ring ? stage_v : (uint16_t*)cache->v;
   ra.B = batch;
   ra.S = seq_len;
-  ra.Hq = Hq;
   ra.Hkv = Hkv;
   ra.dst_rows = ring ? L.stage_rows : cache->capacity;
   ra.r = r;
-  ra.theta = desc->rope_theta;
+  fill_inv_freq(desc->rope_theta, r, ra.inv_freq);
   PrefillAttnArgs aa{};
   for (int b = 0; b < batch; ++b) {
     const int hist = ring ? std::min(start_pos[b], w - 1) : 0;
@@ -295,11 +303,12 @@ int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k, co
     aa.key_pos0[b] = ring ? start_pos[b] - hist : 0;
     aa.n_keys[b] = ring ? hist + seq_len : start_pos[b] + seq_len;
   }
-  hipError_t e = launch_prefill_rope(ra, stream);
+  hipError_t e = launch_prefill_prep(ra, stream);
   if (e != hipSuccess) return HATTN_ERR_LAUNCH;
 
-  // 3. attention over the linear key rows
-  aa.qhat = qhat;
+  // 3. attention over the linear key rows (queries rotated in the kernel)
+  aa.q = (const uint16_t*)q;
+  aa.table = table;
   aa.kc = ring ? stage_k : (const uint16_t*)cache->k;
   aa.vc = ring ? stage_v : (const uint16_t*)cache->v;
   aa.gate = (const uint16_t*)gate;
@@ -310,6 +319,7 @@ int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k, co
   aa.Hkv = Hkv;
   aa.rows = ring ? L.stage_rows : cache->capacity;
   aa.window = desc->layer_type == HATTN_LAYER_SLIDING ? w : 0;
+  aa.r = r;
   aa.q_tiles = (seq_len + 31) / 32;
   hipEvent_t prof = profile_begin(HATTN_PROFILE_PREFILL, stream);
   e = launch_prefill_attn(aa, stream);
@@ -385,7 +395,7 @@ int hattn_decode(const hattn_layer_desc* desc, const void* q, const void* k, con
   a.window = desc->layer_type == HATTN_LAYER_SLIDING ? desc->window : 0;
   a.max_pos = max_pos;
   a.r = rotary_channels(desc->rotary_fraction, desc->head_dim);
-  a.theta = desc->rope_theta;
+  fill_inv_freq(desc->rope_theta, a.r, a.inv_freq);
   a.nsplit = p.nsplit;
   a.split_keys = p.split_keys;
   hipEvent_t prof = profile_begin(HATTN_PROFILE_DECODE, stream);

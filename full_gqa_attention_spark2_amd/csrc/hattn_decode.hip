@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     const int d = t;
     const int half = a.r >> 1;
     double c = 1.0, s = 0.0;
-    if (d < a.r) sincos(rope_angle(p, d < half ? d : d - half, a.r, a.theta), &s, &c);
+    if (d < a.r) rope_sincos(p, a.inv_freq[d < half ? d : d - half], &s, &c);
     auto rot = [&](const uint16_t* x) -> double {
       const double xd = (double)bf16_bits_to_float(x[d]);
       if (d >= a.r) return xd;

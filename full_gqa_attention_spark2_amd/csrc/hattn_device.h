@@ -51,10 +51,22 @@ __device__ __forceinline__ uint16_t double_to_bf16_bits(double x) {
 }
 
 // ---------------------------------------------------------------- RoPE
-// Angle of pair i at position p: p * theta^(-2i/r), in fp64.
-__device__ __forceinline__ double rope_angle(int pos, int i, int r, double theta) {
-  double inv_freq = pow(theta, -2.0 * (double)i / (double)r);
-  return (double)pos * inv_freq;
+// cos and sin of the fp64 angle p * inv_freq. The angle is reduced by 2*pi
+// with a three-part Cody-Waite split (24 + 24 + 53 bits; exact for the
+// quotients |k| < 2^28 that positions below 2^30 produce), then evaluated in
+// fp64 on [-pi, pi]. inv_freq_i = theta^(-2i/r) is computed on the host.
+constexpr double kTwoPiHi = 0x1.921fb6p+2;
+constexpr double kTwoPiMid = -0x1.777a5cp-23;
+constexpr double kTwoPiLo = -0x1.ee59d9cceba40p-48;
+constexpr double kInvTwoPi = 0x1.45f306dc9c883p-3;
+
+__device__ __forceinline__ void rope_sincos(int pos, double inv_freq, double* s, double* c) {
+  const double ang = (double)pos * inv_freq;
+  const double k = rint(ang * kInvTwoPi);
+  double r = fma(-k, kTwoPiHi, ang);
+  r = fma(-k, kTwoPiMid, r);
+  r = fma(-k, kTwoPiLo, r);
+  sincos(r, s, c);
 }
 
 // ---------------------------------------------------------------- masks

@@ -10,20 +10,19 @@ namespace hattn {
 
 constexpr int kMaxPrefillBatch = 128;
 
-// Token-wise RoPE of the new prefill tokens: rotated Q -> qhat (bf16
-// [B][S][Hq][256]), rotated K and V -> key/value rows of dst (a cache or the
-// staging buffer, [B][Hkv][rows][256]).
-struct PrefillRopeArgs {
-  const uint16_t* q;
+// Per new prefill token: cos/sin of its RoPE angles (fp32 table for the
+// attention kernel's query rotation) and its rotated key and value, written
+// as rows of dst (a cache or the staging buffer, [B][Hkv][rows][256]).
+struct PrefillPrepArgs {
   const uint16_t* k;
   const uint16_t* v;
-  uint16_t* qhat;
+  float2* table;    // [B][S][r/2] (cos, sin)
   uint16_t* dst_k;
   uint16_t* dst_v;
-  int B, S, Hq, Hkv;
+  int B, S, Hkv;
   int dst_rows;     // rows per (b, kv head) in dst
   int r;            // rotated channels
-  double theta;
+  double inv_freq[128];
   int start[kMaxPrefillBatch];    // position of token 0 of sequence b
   int dst_row0[kMaxPrefillBatch]; // dst row of token 0 of sequence b
 };
@@ -41,7 +40,8 @@ struct RingCopyArgs {
 };
 
 struct PrefillAttnArgs {
-  const uint16_t* qhat;   // bf16 [B][S][Hq][256], rotated
+  const uint16_t* q;      // bf16 [B][S][Hq][256], before RoPE
+  const float2* table;    // [B][S][r/2] cos/sin of the query positions
   const uint16_t* kc;     // bf16 [B][Hkv][rows][256], rotated keys
   const uint16_t* vc;
   const uint16_t* gate;   // bf16 [B][S][Hq]
@@ -49,6 +49,7 @@ struct PrefillAttnArgs {
   int B, S, Hq, Hkv;
   int rows;               // rows per (b, kv head) in kc / vc
   int window;             // <= 0: unbounded
+  int r;                  // rotated channels (multiple of 16)
   int q_tiles;            // ceil(S / 32)
   int start[kMaxPrefillBatch];     // position of query 0
   int key_pos0[kMaxPrefillBatch];  // position held by key row 0
@@ -68,16 +69,16 @@ struct DecodeArgs {
   float* part_ml;         // [B][Hq][nsplit][2]
   int B, Hq, Hkv, cap, ring, window, max_pos;
   int r;
-  double theta;
   int nsplit;
   int split_keys;         // keys per split, multiple of 128
+  double inv_freq[128];
 };
 
 struct RopeApplyArgs {
   uint16_t* x;
   const int* pos;
   int n_tok, n_heads, head_dim, r;
-  double theta;
+  double inv_freq[256];
 };
 
 struct ProbeArgs {
@@ -87,7 +88,7 @@ struct ProbeArgs {
   int ring, cap, window, q_pos0, n_q;
 };
 
-hipError_t launch_prefill_rope(const PrefillRopeArgs& a, hipStream_t s);
+hipError_t launch_prefill_prep(const PrefillPrepArgs& a, hipStream_t s);
 hipError_t launch_ring_to_stage(const RingCopyArgs& a, hipStream_t s);
 hipError_t launch_stage_to_ring(const RingCopyArgs& a, hipStream_t s);
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s);

@@ -3,7 +3,8 @@
 // sliding layers keep the last 512 tokens).
 //
 // Angles are p * theta^(-2i/r) in fp64 and cos/sin are evaluated in fp64; the
-// rotation runs in fp64 and each rotated value is rounded once to bf16.
+// rotation of stored keys runs in fp64 and each rotated value is rounded once
+// to bf16.
 #include "hattn_device.h"
 #include "hattn_internal.h"
 
@@ -26,7 +27,9 @@ __device__ __forceinline__ uint16_t rotate_channel(const uint16_t* x, int d, int
   return double_to_bf16_bits(y);
 }
 
-__global__ __launch_bounds__(256) void prefill_rope_kernel(PrefillRopeArgs a) {
+// One block per (new token, sequence): the token's cos/sin table row, its
+// rotated keys (fp64 rotation, one bf16 rounding) and its values.
+__global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillPrepArgs a) {
   __shared__ double cs[128];
   __shared__ double sn[128];
   const int i = blockIdx.x;
@@ -36,23 +39,23 @@ __global__ __launch_bounds__(256) void prefill_rope_kernel(PrefillRopeArgs a) {
   const int half = a.r >> 1;
   if (t < half) {
     double s, c;
-    sincos(rope_angle(p, t, a.r, a.theta), &s, &c);
+    rope_sincos(p, a.inv_freq[t], &s, &c);
     cs[t] = c;
     sn[t] = s;
+    a.table[((size_t)b * a.S + i) * half + t] = make_float2((float)c, (float)s);
   }
   __syncthreads();
-  const size_t qbase = ((size_t)b * a.S + i) * a.Hq * kHeadDim;
-  for (int e = t; e < a.Hq * kHeadDim; e += 256) {
-    const int h = e >> 8, d = e & 255;
-    a.qhat[qbase + e] = rotate_channel(a.q + qbase + (size_t)h * kHeadDim, d, half, a.r, cs, sn);
-  }
   const size_t kbase = ((size_t)b * a.S + i) * a.Hkv * kHeadDim;
   const int row = a.dst_row0[b] + i;
   for (int e = t; e < a.Hkv * kHeadDim; e += 256) {
     const int h = e >> 8, d = e & 255;
     const size_t o = (((size_t)b * a.Hkv + h) * a.dst_rows + row) * kHeadDim + d;
     a.dst_k[o] = rotate_channel(a.k + kbase + (size_t)h * kHeadDim, d, half, a.r, cs, sn);
-    a.dst_v[o] = a.v[kbase + e];
+  }
+  for (int c = t; c < a.Hkv * 32; c += 256) {  // values: 16-byte chunks
+    const int h = c >> 5, ch = c & 31;
+    const size_t o = (((size_t)b * a.Hkv + h) * a.dst_rows + row) * kHeadDim;
+    ((uint4*)(a.dst_v + o))[ch] = ((const uint4*)(a.v + kbase + (size_t)h * kHeadDim))[ch];
   }
 }
 
@@ -86,7 +89,7 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(RopeApplyArgs a) {
   const int p = a.pos[tok];
   for (int i = threadIdx.x; i < half; i += 256) {
     double s, c;
-    sincos(rope_angle(p, i, a.r, a.theta), &s, &c);
+    rope_sincos(p, a.inv_freq[i], &s, &c);
     cs[i] = c;
     sn[i] = s;
   }
@@ -113,8 +116,8 @@ __global__ __launch_bounds__(256) void index_probe_kernel(ProbeArgs a) {
   }
 }
 
-hipError_t launch_prefill_rope(const PrefillRopeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(prefill_rope_kernel, dim3(a.S, a.B), dim3(256), 0, s, a);
+hipError_t launch_prefill_prep(const PrefillPrepArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(prefill_prep_kernel, dim3(a.S, a.B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

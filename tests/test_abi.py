@@ -124,11 +124,11 @@ def test_workspace_sizes(L):
     sl = hb.layer_desc("sliding")
     lin = hb.KvCacheC(FAKE, FAKE, hb.KV_LINEAR, 1, 8192)
     ring = hb.KvCacheC(FAKE, FAKE, hb.KV_RING, 1, 512)
-    # linear prefill: only the rotated Q
-    assert L.hattn_prefill_workspace_size(ctypes.byref(fu), ctypes.byref(lin), 1, 8192) == 8192 * 16 * 256 * 2
-    # ring prefill: rotated Q plus K/V staging of (window - 1 + S) rows
+    # linear prefill: only the cos/sin table of the new positions (r/2 pairs of fp32)
+    assert L.hattn_prefill_workspace_size(ctypes.byref(fu), ctypes.byref(lin), 1, 8192) == 8192 * 32 * 8
+    # ring prefill: the table plus K/V staging of (window - 1 + S) rows
     got = L.hattn_prefill_workspace_size(ctypes.byref(sl), ctypes.byref(ring), 1, 1024)
-    assert got == 1024 * 16 * 256 * 2 + 2 * 4 * (511 + 1024) * 256 * 2
+    assert got == 1024 * 128 * 8 + 2 * 4 * (511 + 1024) * 256 * 2
     # decode over a 2^20-token linear cache needs split partials
     big = hb.KvCacheC(FAKE, FAKE, hb.KV_LINEAR, 1, 1 << 20)
     assert L.hattn_decode_workspace_size(ctypes.byref(fu), ctypes.byref(big), 1) >= 16 * 2 * 256 * 4
