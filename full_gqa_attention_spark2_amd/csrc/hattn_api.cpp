@@ -320,7 +320,7 @@ int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k, co
   aa.rows = ring ? L.stage_rows : cache->capacity;
   aa.window = desc->layer_type == HATTN_LAYER_SLIDING ? w : 0;
   aa.r = r;
-  aa.q_tiles = (seq_len + 31) / 32;
+  aa.q_tiles = (seq_len + kPrefillBlockQ - 1) / kPrefillBlockQ;
   hipEvent_t prof = profile_begin(HATTN_PROFILE_PREFILL, stream);
   e = launch_prefill_attn(aa, stream);
   profile_end(prof, stream);

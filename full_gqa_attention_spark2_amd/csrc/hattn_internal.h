@@ -9,6 +9,7 @@
 namespace hattn {
 
 constexpr int kMaxPrefillBatch = 128;
+constexpr int kPrefillBlockQ = 32;   // query positions per prefill workgroup
 
 // Per new prefill token: cos/sin of its RoPE angles (fp32 table for the
 // attention kernel's query rotation) and its rotated key and value, written
@@ -50,7 +51,7 @@ struct PrefillAttnArgs {
   int rows;               // rows per (b, kv head) in kc / vc
   int window;             // <= 0: unbounded
   int r;                  // rotated channels (multiple of 16)
-  int q_tiles;            // ceil(S / 32)
+  int q_tiles;            // ceil(S / kPrefillBlockQ)
   int start[kMaxPrefillBatch];     // position of query 0
   int key_pos0[kMaxPrefillBatch];  // position held by key row 0
   int n_keys[kMaxPrefillBatch];    // valid key rows

@@ -17,10 +17,14 @@
 // K and V tiles go from global memory straight into LDS (global_load_lds,
 // 16 B per lane) in the order the MFMA reads them, so every LDS read is a
 // contiguous, conflict-free 512 B per half-wave at "lane base + constant".
-// Two K slots and two V slots form a pipeline: while tile t's softmax and
-// P.V run, S for tile t+1 is computed and tiles t+1 (V) and t+2 (K) load.
-// The running max is only moved (and O rescaled) when a tile's max exceeds it
-// by more than 2^8, so most tiles skip the rescale.
+// Two K slots and two V slots form a pipeline: step t computes S(t) and
+// issues P(t-1).V(t-1), so the softmax of tile t (VALU) runs while the
+// matrix cores work on P.V of tile t-1, and tiles t+1 (K) and t (V) load
+// meanwhile. The running max is only moved (and O rescaled) when a tile's max
+// exceeds it by more than 2^8, so most tiles skip the rescale; the step body
+// has no branch between its MFMAs and its softmax.
+#include <type_traits>
+
 #include "hattn_device.h"
 #include "hattn_internal.h"
 
@@ -28,7 +32,7 @@ namespace hattn {
 
 namespace {
 
-constexpr int kBM = 32;                          // query positions per workgroup
+constexpr int kBM = kPrefillBlockQ;              // query positions per workgroup
 constexpr int kBN = 64;                          // keys per tile
 constexpr int kTileBytes = kBN * kHeadDim * 2;   // 32 KiB: one K or V tile
 constexpr float kScoreScale = kLog2e / 16.0f;    // 1/sqrt(256), in log2 units
@@ -81,7 +85,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   const int kvh = r2 % a.Hkv;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = kvh * kGroup + wave;
   const int q0 = qt * kBM;
   const int nq = min(kBM, a.S - q0);
@@ -96,31 +100,31 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   const int nt = (row_hi + kBN - 1) / kBN - t_lo;
 
   const size_t kv_off = ((size_t)b * a.Hkv + kvh) * (size_t)a.rows * kHeadDim;
-  const uint16_t* kbase = a.kc + kv_off;
-  const uint16_t* vbase = a.vc + kv_off;
+  const char* kbase = (const char*)(a.kc + kv_off);
+  const char* vbase = (const char*)(a.vc + kv_off);
 
   // Each wave stages 8 of the 32 K blocks and 8 of the 32 V blocks of a
   // tile. Rows past the valid keys re-read the last valid key; their scores
   // are masked, so they contribute exactly zero.
-  auto load_k = [&](int t, char* slot) {
+  const int v_lane_key = 8 * (lane >> 5) + 4 * ((lane >> 4) & 1) + ((lane >> 1) & 3);
+  const int v_lane_col = 32 * ((lane >> 3) & 1) + 16 * (lane & 1);  // bytes
+  auto load_k = [&](int t, char* slot) __attribute__((always_inline)) {
     char* dst = slot + wave * 8 * 1024;
-    const int row = min(t * kBN + lane, nk - 1);
-    const uint16_t* src = kbase + (size_t)row * kHeadDim + wave * 64;
+    const uint32_t off = (uint32_t)min(t * kBN + lane, nk - 1) * 512u + (uint32_t)wave * 128u;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) load_lds16(src + u * 8, dst + u * 1024);
+    for (int u = 0; u < 8; ++u) load_lds16(kbase + off + u * 16, dst + u * 1024);
   };
-  auto load_v = [&](int t, char* slot) {
+  auto load_v = [&](int t, char* slot) __attribute__((always_inline)) {
     char* dst = slot + wave * 8 * 1024;
-    const int key = t * kBN + 16 * wave + 8 * (lane >> 5) + 4 * ((lane >> 4) & 1) + ((lane >> 1) & 3);
-    const uint16_t* src = vbase + (size_t)min(key, nk - 1) * kHeadDim + 16 * ((lane >> 3) & 1) + 8 * (lane & 1);
+    const uint32_t off = (uint32_t)min(t * kBN + 16 * wave + v_lane_key, nk - 1) * 512u + (uint32_t)v_lane_col;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) load_lds16(src + db * 32, dst + db * 1024);
+    for (int db = 0; db < 8; ++db) load_lds16(vbase + off + db * 64, dst + db * 1024);
   };
 
   // Start the first tiles moving before the query prologue.
   load_k(t_lo, k_lds0);
-  load_v(t_lo, v_lds0);
   if (nt > 1) load_k(t_lo + 1, k_lds1);
+  load_v(t_lo, v_lds0);
 
   // ---- queries: RoPE in fp32 from the cos/sin table, then bf16 fragments
   // (B operand of S^T): lane holds query lane % 32, channels
@@ -154,28 +158,58 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
       for (int j = 0; j < 8; ++j) v[j] = (__bf16)(qvalid ? x[j] : 0.f);
       qf[ks] = v;
     }
+    // The fragments are only ever MFMA operands: keep them in the
+    // accumulation registers, which leaves the VGPRs to the softmax.
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) asm volatile("" : "+a"(qf[ks]));
   }
 
-  auto compute_s = [&](const char* kt, f32x16& s0, f32x16& s1) {
-    const char* base = kt + (lane >> 5) * 1024 + (lane & 31) * 16;
-    s0 = f32x16{};
-    s1 = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      const bf16x8 a0 = *(const bf16x8*)(base + ks * 2048);
-      const bf16x8 a1 = *(const bf16x8*)(base + ks * 2048 + 512);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
-    }
-  };
-  auto need_mask = [&](int t) {
+  auto need_mask = [&](int t) __attribute__((always_inline)) {
     const int row0 = t * kBN;
     return (kp0 + row0 + kBN - 1 > pq_first) || (a.window > 0 && kp0 + row0 <= pq_last - a.window) ||
            (row0 + kBN > nk);
   };
-  // Register i of block kb holds key row t*64 + kb*32 + 8*(i/4) + 4*(lane/32)
-  // + i%4 for query lane % 32.
-  auto mask_s = [&](int t, f32x16& s0, f32x16& s1) {
+
+  f32x16 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = f32x16{};
+  float m_i = -1e30f;  // running max (log2 units) of this lane's query
+  float l_i = 0.f;     // running sum
+
+  // V^T fragments: lane (16g + i) of a transposed read gets channel
+  // 32db + 16(g%2) + i of keys 16tt + 8j2 + 4(g/2) + 0..3, which are the key
+  // slots (g/2)*8 + 4*j2 + 0..3 of the P^T fragment.
+  const int tr_off = lane * 8;
+  // P.V with the V^T fragments read 3 MFMAs ahead of their use, so LDS
+  // latency hides behind the matrix cores.
+  auto pv = [&](const char* vslot, const bf16x8* p) __attribute__((always_inline)) {
+    const char* vt = vslot + tr_off;
+    constexpr int kAhead = 3;
+    s16x4 vl[kAhead + 1], vh[kAhead + 1];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) {
+      vl[i] = lds_read_tr(vt + i * 1024);
+      vh[i] = lds_read_tr(vt + i * 1024 + 512);
+    }
+#pragma unroll
+    for (int n = 0; n < 32; ++n) {  // n = tt*8 + db
+      if (n + kAhead < 32) {
+        vl[(n + kAhead) % (kAhead + 1)] = lds_read_tr(vt + (n + kAhead) * 1024);
+        vh[(n + kAhead) % (kAhead + 1)] = lds_read_tr(vt + (n + kAhead) * 1024 + 512);
+      }
+      const s16x8 both = __builtin_shufflevector(vl[n % (kAhead + 1)], vh[n % (kAhead + 1)], 0, 1, 2, 3, 4, 5, 6, 7);
+      acc[n & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), p[n >> 3], acc[n & 7], 0, 0, 0);
+    }
+    // Keep O resident in the accumulation registers between tiles (the
+    // register allocator otherwise parks it in VGPRs and copies it every
+    // tile).
+#pragma unroll
+    for (int db = 0; db < 8; ++db) asm volatile("" : "+a"(acc[db]));
+  };
+
+  // Mask of tile t's scores. Register i of block kb holds key row
+  // t*64 + kb*32 + 8*(i/4) + 4*(lane/32) + i%4 for query lane % 32.
+  auto mask_s = [&](int t, f32x16& s0, f32x16& s1) __attribute__((always_inline)) {
     const int pq = pq_first + (lane & 31);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -186,92 +220,122 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
       s1[i] = ok1 ? s1[i] : -__builtin_inff();
     }
   };
-
-  f32x16 acc[8];
+  // S^T with the K fragments read 3 k-steps ahead of their use.
+  auto compute_s = [&](const char* kslot, f32x16& s0, f32x16& s1) __attribute__((always_inline)) {
+    const char* base = kslot + (lane >> 5) * 1024 + (lane & 31) * 16;
+    constexpr int kAhead = 3;
+    bf16x8 fa[kAhead + 1], fb[kAhead + 1];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = f32x16{};
-  float m_i = -1e30f;  // running max (log2 units) of this lane's query
-  float l_i = 0.f;     // running sum
-
-  wait_loads();
-  __syncthreads();
-  f32x16 sc0, sc1;
-  compute_s(k_lds0, sc0, sc1);
-  if (need_mask(t_lo)) mask_s(t_lo, sc0, sc1);
-
-  // V^T fragments: lane (16g + i) of a transposed read gets channel
-  // 32db + 16(g%2) + i of keys 16tt + 8j2 + 4(g/2) + 0..3, which are the key
-  // slots (g/2)*8 + 4*j2 + 0..3 the P^T fragment below uses.
-  const int tr_off = lane * 8;
-
-  // One pipeline step for tile t = t_lo + j. Slots: kn holds K(t+1), vc holds
-  // V(t); K(t+2) goes to kf and V(t+1) to vf, the slots step j-1 read.
-  auto step = [&](int j, const char* kn, const char* vc, char* kf, char* vf) {
-    const int t = t_lo + j;
-    wait_loads();
-    __syncthreads();
-    if (j + 1 < nt) load_v(t + 1, vf);
-    if (j + 2 < nt) load_k(t + 2, kf);
-
-    // ---- running max of tile t; rescale only when it grows by > 2^8
-    float mx = fmaxf(sc0[0], sc1[0]);
+    for (int i = 0; i < kAhead; ++i) {
+      fa[i] = *(const bf16x8*)(base + i * 2048);
+      fb[i] = *(const bf16x8*)(base + i * 2048 + 512);
+    }
+    s0 = f32x16{};
+    s1 = f32x16{};
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(sc0[i], sc1[i]));
+    for (int ks = 0; ks < 16; ++ks) {
+      if (ks + kAhead < 16) {
+        fa[(ks + kAhead) % (kAhead + 1)] = *(const bf16x8*)(base + (ks + kAhead) * 2048);
+        fb[(ks + kAhead) % (kAhead + 1)] = *(const bf16x8*)(base + (ks + kAhead) * 2048 + 512);
+      }
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks % (kAhead + 1)], qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks % (kAhead + 1)], qf[ks], s1, 0, 0, 0);
+    }
+    // scores feed VALU code: produce them in VGPRs
+    asm volatile("" : "+v"(s0), "+v"(s1));
+  };
+  // Softmax of one tile's scores into pb. The running max moves only when
+  // the tile's max exceeds it by more than 2^8; returns the factor O must be
+  // rescaled by (1 when the max did not move).
+  auto softmax = [&](f32x16& s0, f32x16& s1, bf16x8* pb) __attribute__((always_inline)) {
+    float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
     mx = fmaxf(mx, wave_shfl_xor(mx, 32)) * kScoreScale;
     const float m_new = fmaxf(m_i, mx);
-    if (__any(m_new > m_i + kRescaleSlack)) {
-      const float alpha = fast_exp2(m_i - m_new);
-      l_i *= alpha;
-#pragma unroll
-      for (int db = 0; db < 8; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-      m_i = m_new;
-    }
-
-    // ---- S for tile t+1 (on the last tile this reads a stale slot and is
-    // discarded); independent of the softmax below, so the two interleave.
-    f32x16 sn0, sn1;
-    compute_s(kn, sn0, sn1);
-
-    // ---- probabilities of tile t and P^T fragments: step tt covers keys
-    // 16tt .. +15; key slot (lane/32)*8 + j of the step is register
-    // 8*(tt%2) + j of block tt/2.
+    const bool rescale = __any(m_new > m_i + kRescaleSlack);
+    const float m_use = rescale ? m_new : m_i;
+    const float alpha = fast_exp2(m_i - m_use);
+    // step tt of P^T covers keys 16tt .. +15; its key slot (lane/32)*8 + j
+    // is register 8*(tt%2) + j of block tt/2
     float rs = 0.f;
-    bf16x8 pb[4];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float p0 = fast_exp2(fmaf(sc0[i], kScoreScale, -m_i));
-      const float p1 = fast_exp2(fmaf(sc1[i], kScoreScale, -m_i));
+      const float p0 = fast_exp2(fmaf(s0[i], kScoreScale, -m_use));
+      const float p1 = fast_exp2(fmaf(s1[i], kScoreScale, -m_use));
       rs += p0 + p1;
       pb[i >> 3][i & 7] = (__bf16)p0;
       pb[2 + (i >> 3)][i & 7] = (__bf16)p1;
     }
     rs += wave_shfl_xor(rs, 32);
-    l_i += rs;
-
-    // ---- O^T += V^T P^T for tile t
-    const char* vt = vc + tr_off;
+    l_i = l_i * alpha + rs;
+    m_i = m_use;
+    return rescale ? alpha : 1.0f;
+  };
+  // O *= alpha in place in the accumulation registers (read, multiply,
+  // write back per element), so O never has to move to VGPRs.
+  auto rescale_o = [&](float alpha) __attribute__((always_inline)) {
+    if (alpha != 1.0f) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+      for (int db = 0; db < 8; ++db)
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const char* blk = vt + (tt * 8 + db) * 1024;
-        const s16x4 lo = lds_read_tr(blk);
-        const s16x4 hi = lds_read_tr(blk + 512);
-        const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pb[tt], acc[db], 0, 0, 0);
-      }
-
-    if (j + 1 < nt && need_mask(t + 1)) mask_s(t + 1, sn0, sn1);
-    sc0 = sn0;
-    sc1 = sn1;
+        for (int i = 0; i < 16; ++i) {
+          float tmp;
+          asm volatile(
+              "v_accvgpr_read_b32 %1, %0\n\t"
+              "v_mul_f32 %1, %1, %2\n\t"
+              "v_accvgpr_write_b32 %0, %1"
+              : "+a"(acc[db][i]), "=&v"(tmp)
+              : "v"(alpha));
+        }
+    }
   };
 
-  for (int j = 0; j < nt; j += 2) {
-    step(j, k_lds1, v_lds0, k_lds0, v_lds1);
-    if (j + 1 < nt) step(j + 1, k_lds0, v_lds1, k_lds1, v_lds0);
+  // Iteration j (tile t = t_lo + j) overlaps three things: the softmax of
+  // S(t) (VALU), S(t+1) = K(t+1) Q^T and P(t-1).V(t-1) (MFMA), and the loads
+  // of K(t+2) and V(t). Tile j's K lives in k_lds[j % 2] and its V in
+  // v_lds[j % 2]; the score and probability registers alternate the same
+  // way, so every slot and register set is fixed at compile time.
+  load_k(t_lo, k_lds0);
+  if (nt > 1) load_k(t_lo + 1, k_lds1);
+  f32x16 sA0, sA1, sB0, sB1;  // scores of even / odd tiles
+  bf16x8 pA[4], pB[4];        // probabilities of even / odd tiles
+  wait_loads();
+  __syncthreads();
+  compute_s(k_lds0, sA0, sA1);
+  if (need_mask(t_lo)) mask_s(t_lo, sA0, sA1);
+
+  // One iteration; kPv is false only for the first tile. On the last tile
+  // S(t+1) is computed from a stale slot and discarded, which keeps the body
+  // free of branches between its MFMAs and its softmax.
+  auto step = [&](auto has_pv, int j, const char* kn, const char* vp, char* kf, char* vf, f32x16& sc0,
+                  f32x16& sc1, f32x16& sn0, f32x16& sn1, const bf16x8* pp,
+                  bf16x8* pn) __attribute__((always_inline)) {
+    constexpr bool kPv = decltype(has_pv)::value;
+    const int t = t_lo + j;
+    wait_loads();
+    __syncthreads();
+    if (j + 2 < nt) load_k(t + 2, kf);
+    load_v(t, vf);
+    compute_s(kn, sn0, sn1);
+    if (kPv) pv(vp, pp);
+    const float alpha = softmax(sc0, sc1, pn);
+    rescale_o(alpha);
+    if (j + 1 < nt && need_mask(t + 1)) mask_s(t + 1, sn0, sn1);
+  };
+  using T_ = std::integral_constant<bool, true>;
+  using F_ = std::integral_constant<bool, false>;
+  // even j: S(t) in sA, P(t) -> pA, P(t-1) in pB; odd j: the other way round
+  step(F_{}, 0, k_lds1, v_lds1, k_lds0, v_lds0, sA0, sA1, sB0, sB1, pB, pA);
+  for (int j = 1; j < nt; j += 2) {
+    step(T_{}, j, k_lds0, v_lds0, k_lds1, v_lds1, sB0, sB1, sA0, sA1, pA, pB);
+    if (j + 1 < nt) step(T_{}, j + 1, k_lds1, v_lds1, k_lds0, v_lds0, sA0, sA1, sB0, sB1, pB, pA);
   }
+  // P.V of the last tile
+  wait_loads();
+  __syncthreads();
+  if ((nt - 1) & 1) pv(v_lds1, pB);
+  else pv(v_lds0, pA);
 
   // ---- epilogue: divide by the softmax sum, gate in fp32, one bf16 store.
   // acc[db] register i holds channel db*32 + 8*(i/4) + 4*(lane/32) + i%4.
