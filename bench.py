@@ -13,9 +13,9 @@ divided by the event-timed duration of the K timed calls.
 Decode is timed in its own section after the prefill steps and reported under
 "decode": sliding-layer decode over 64 sequences with 512-slot ring caches,
 and full-layer decode over 2^20 cached tokens (batch 1) and 8 x 131072
-tokens, each as KV GB/s of the attention kernels. Before every timed decode
-call a 1 GiB buffer is read so the 256 MB last-level cache cannot serve the
-KV cache.
+tokens, each as KV GB/s per call (decode kernel plus split merge, timed
+back to back). The calls cycle over enough distinct caches that the 256 MB
+last-level cache cannot serve the KV cache.
 
 All inputs are seeded synthetic tensors (N(0,1) bf16 Q/K/V and caches, gate
 logits N(0, 2^2)) already resident in HBM when timing starts.
@@ -60,39 +60,58 @@ def source_sha(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def counter_traffic(name, kernel):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, or
-    None when it is missing or the kernel source changed since."""
-    p = os.path.join(PROFILES, name)
+def counter_traffic(workload):
+    """HBM bytes per launch of a workload's dominant kernel, from the committed
+    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the same
+    counters on a copy of known size), or None when the summary is missing or
+    the kernel's source has changed since it was taken."""
+    p = os.path.join(PROFILES, "hbm_traffic_counters.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         d = json.load(f)
-    if d.get("kernel_source_sha256") != source_sha(KERNEL_SRC[kernel]):
+    e = d.get("workloads", {}).get(workload)
+    if not e or e.get("source_sha256") != source_sha(KERNEL_SRC[e["source"]]):
         return None
-    return d.get("hbm_bytes_per_launch")
+    return e.get("hbm_bytes_per_launch")
 
 
-def time_calls(torch, fn, steps, warmup, before=None):
+def copy_calibration():
+    """A plain device copy of known size (fp32 negation, 1 GiB read + 1 GiB
+    written per launch), run under the same counters as the kernels to scale
+    FETCH_SIZE / WRITE_SIZE to bytes."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    return {"kernel": "torch.neg fp32", "bytes_read_per_launch": 4 * n, "bytes_written_per_launch": 4 * n,
+            "launches": 3}
+
+
+def time_calls(torch, fn, steps, warmup):
     for _ in range(warmup):
-        if before:
-            before()
         fn()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
-        if before:
-            before()
         fn()
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
 
 
-def cpu_baseline(S=8192, n_rows=512):
-    """The fp64 oracle on a sample of the headline workload, on host cores."""
+def cpu_baseline(S=8192, budget_s=12.0):
+    """The fp64 oracle on a bounded sample of the headline workload, on host
+    cores: interleaved sets of 512 evenly spaced query rows (rows k, k+16,
+    k+32, ... for k = 0, 1, ...) until about ``budget_s`` seconds of CPU work
+    are done or every row is covered."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -100,21 +119,28 @@ def cpu_baseline(S=8192, n_rows=512):
     from oracle import hattn_oracle as O
 
     inp = synth.prefill_inputs(1, S, 16, 4, seed=0)
-    rows = np.linspace(0, S - 1, n_rows).astype(np.int64)
+    stride = 16
+    done_rows = 0
+    flops = 0
     t0 = time.perf_counter()
-    O.prefill_ref(inp["q"], inp["k"], inp["v"], inp["gate"], [0], window=None, theta=5e6, rotary_fraction=0.25,
-                  rows=rows)
+    for k in range(stride):
+        rows = np.arange(k, S, stride, dtype=np.int64)
+        O.prefill_ref(inp["q"], inp["k"], inp["v"], inp["gate"], [0], window=None, theta=5e6,
+                      rotary_fraction=0.25, rows=rows)
+        done_rows += len(rows)
+        flops += 4 * 256 * 16 * int((rows + 1).sum())
+        if time.perf_counter() - t0 >= budget_s:
+            break
     dt = time.perf_counter() - t0
-    flops = 4 * 256 * 16 * int(sum(int(r) + 1 for r in rows))
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{n_rows} evenly spaced query rows (all 16 heads, {flops / 1e9:.1f} GFLOP) of the "
-                  f"S={S} full-layer prefill, fp64 numpy, {dt:.1f} s on {len(os.sched_getaffinity(0))} "
-                  f"visible host cores",
+        "sample": f"{done_rows} of the {S} query rows (interleaved sets of {S // stride} evenly spaced rows, "
+                  f"all 16 heads, {flops / 1e9:.1f} GFLOP) of the full-layer prefill, fp64 numpy, "
+                  f"{dt:.1f} s on {len(os.sched_getaffinity(0))} visible host cores",
     }
 
 
@@ -157,67 +183,67 @@ def run(args):
     roofline = {
         "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-        "traffic": counter_traffic("prefill_attn_full_s8192_counters.json", "prefill"),
+        "traffic": counter_traffic("prefill_full_s8192"),
         "kernel": "prefill_attn_kernel", "flop_per_launch": flops, "avg_launch_ms": round(attn_ms, 5),
     }
     del inp, cache, out, ws
     torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- decode
+    # Each decode workload is timed as K back-to-back calls (decode kernel and
+    # split merge) between one event pair. Calls cycle over enough distinct KV
+    # caches (>= 1 GiB in total) that the 256 MB last-level cache cannot
+    # serve a call's KV from the previous ones.
     decode = None
     if not args.skip_decode:
         decode = {}
-        # Reading 1 GiB between calls evicts the KV cache from the 256 MB
-        # last-level cache without leaving dirty lines behind.
-        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        sink = torch.empty((), dtype=torch.float32, device=dev)
 
-        def flush_llc():
-            torch.sum(flush, dim=0, out=sink)
-
-        def decode_case(tag, desc, B, cap, kind, pos, ck, cv):
+        def decode_case(tag, desc, B, cap, kind, pos, caches):
             dinp = {k: v.to(dev) for k, v in synth.decode_inputs(B, Hq, Hkv, seed=1).items()}
             pos_d = torch.as_tensor(pos, dtype=torch.int32).to(dev)
-            c = hb.KVCache(ck, cv, kind)
             o = torch.empty_like(dinp["q"])
-            wsd = torch.empty(max(hb.decode_workspace_size(desc, c, B), 256), dtype=torch.uint8, device=dev)
             maxp = int(max(pos))
+            cs = [hb.KVCache(ck, cv, kind) for ck, cv in caches]
+            wsd = torch.empty(max(hb.decode_workspace_size(desc, cs[0], B), 256), dtype=torch.uint8, device=dev)
+            it = [0]
 
             def call():
+                c = cs[it[0] % len(cs)]
+                it[0] += 1
                 hb.hattn_decode(desc, dinp["q"], dinp["k"], dinp["v"], dinp["gate"], pos_d, maxp, c, out=o,
                                 workspace=wsd)
 
-            hb.hattn_profile_read(hb.PROFILE_DECODE)
-            hb.hattn_profile_enable(True)
-            ms_call = time_calls(torch, call, args.steps, args.warmup, before=flush_llc)
-            hb.hattn_profile_enable(False)
-            n, tot = hb.hattn_profile_read(hb.PROFILE_DECODE)
-            k_ms = tot / max(n, 1)
+            steps = max(args.steps, 2 * len(cs))
+            ms_call = time_calls(torch, call, steps, args.warmup)
             win = min(cap, 512) if kind == "ring" else None
             toks = sum(min(p + 1, win) if win else p + 1 for p in pos)
             kv_bytes = toks * Hkv * 256 * 2 * 2
-            gbps = kv_bytes / (k_ms * 1e-3) / 1e9
-            log(f"decode {tag}: kernel {k_ms * 1e3:.1f} us ({n} launches), {gbps:.0f} GB/s, "
-                f"{gbps / PEAK_HBM_GBPS * 100:.1f}% of HBM peak")
+            gbps = kv_bytes / (ms_call * 1e-3) / 1e9
+            log(f"decode {tag}: {ms_call * 1e3:.1f} us per call over {steps} calls ({len(cs)} caches), "
+                f"{gbps:.0f} GB/s, {gbps / PEAK_HBM_GBPS * 100:.1f}% of HBM peak")
             decode[tag] = {"GB_per_s": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
-                           "kv_bytes_per_call": kv_bytes, "avg_kernel_us": round(k_ms * 1e3, 2)}
+                           "kv_bytes_per_call": kv_bytes, "avg_call_us": round(ms_call * 1e3, 2),
+                           "calls": steps, "distinct_caches": len(cs),
+                           "traffic": counter_traffic("decode_" + tag)}
 
-        # sliding layer: batch 64, positions uniform in [512, 2^20), 512-slot rings
+        # sliding layer: batch 64, positions uniform in [512, 2^20), 512-slot
+        # rings; eight cache sets of 128 MiB
         pos = synth.positions_uniform(64, 512, 1 << 20, seed=0).tolist()
-        ck = synth.cache_tensor(64, Hkv, 512, seed=100, threads=16).to(dev)
-        cv = synth.cache_tensor(64, Hkv, 512, seed=101, threads=16).to(dev)
-        decode_case("sliding_b64_ring512", hb.layer_desc("sliding", Hq, Hkv), 64, 512, "ring", pos, ck, cv)
-        del ck, cv
-        # full layer: batch 1 at position 2^20 - 1, and batch 8 at 131071 (same 4 GiB of KV)
+        sets = [(synth.cache_tensor(64, Hkv, 512, seed=100 + 2 * i, threads=16).to(dev),
+                 synth.cache_tensor(64, Hkv, 512, seed=101 + 2 * i, threads=16).to(dev)) for i in range(8)]
+        decode_case("sliding_b64_ring512", hb.layer_desc("sliding", Hq, Hkv), 64, 512, "ring", pos, sets)
+        del sets
+        # full layer: batch 1 at position 2^20 - 1, and batch 8 at 131071
+        # (the same 4 GiB of KV, 16x the last-level cache)
         n = 1 << 20
         ck = synth.cache_tensor(1, Hkv, n, seed=200, threads=16).to(dev)
         cv = synth.cache_tensor(1, Hkv, n, seed=201, threads=16).to(dev)
         full = hb.layer_desc("full", Hq, Hkv)
-        decode_case("full_b1_1M", full, 1, n, "linear", [n - 1], ck, cv)
+        decode_case("full_b1_1M", full, 1, n, "linear", [n - 1], [(ck, cv)])
         m = n // 8
-        decode_case("full_b8_131072", full, 8, m, "linear", [m - 1] * 8, ck.view(8, Hkv, m, 256),
-                    cv.view(8, Hkv, m, 256))
-        del ck, cv, flush
+        decode_case("full_b8_131072", full, 8, m, "linear", [m - 1] * 8,
+                    [(ck.view(8, Hkv, m, 256), cv.view(8, Hkv, m, 256))])
+        del ck, cv
         torch.cuda.empty_cache()
 
     line = {
@@ -254,6 +280,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the copy of known size used to scale HBM counters")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); multi-GPU runs are not "
@@ -262,7 +290,7 @@ def main(argv=None):
     if "RANK" in os.environ and os.environ.get("WORLD_SIZE", "1") != "1":
         print("bench.py runs as a single process on one GPU.", file=sys.stderr)
         return 2
-    line = run(args)
+    line = copy_calibration() if args.copy_calibration else run(args)
     print(json.dumps(line), flush=True)
     return 0
 

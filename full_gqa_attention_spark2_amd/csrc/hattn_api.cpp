@@ -247,6 +247,10 @@ int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k, co
     if (s0 < 0 || s0 + seq_len > kMaxPos) return HATTN_ERR_POSITION;
     if (!ring && s0 + seq_len > cache->capacity) return HATTN_ERR_CAPACITY;
   }
+  // The attention kernel addresses a (sequence, KV head) slab of key rows
+  // with 32-bit byte offsets (512 B per row).
+  const long long key_rows = ring ? (long long)desc->window - 1 + seq_len : (long long)cache->capacity;
+  if (key_rows > kMaxPrefillKeyRows) return HATTN_ERR_UNSUPPORTED;
   const PrefillLayout L = prefill_layout(desc, cache, batch, seq_len);
   if (!workspace || workspace_bytes < L.total) return HATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return HATTN_ERR_ALIGN;

@@ -10,6 +10,7 @@ namespace hattn {
 
 constexpr int kMaxPrefillBatch = 128;
 constexpr int kPrefillBlockQ = 32;   // query positions per prefill workgroup
+constexpr long long kMaxPrefillKeyRows = 1LL << 23;  // key rows per (sequence, KV head) slab
 
 // Per new prefill token: cos/sin of its RoPE angles (fp32 table for the
 // attention kernel's query rotation) and its rotated key and value, written

@@ -121,7 +121,10 @@ size_t hattn_prefill_workspace_size(const hattn_layer_desc* desc,
  *     cache must hold positions up to start_pos[b]-1 as ring slots.
  *   out:  bf16 [B][S][num_q_heads][256]; must not alias any input.
  * The rotated keys and the values of the new tokens are written to the cache
- * (a ring keeps the last min(S, capacity) of them). B <= 128. */
+ * (a ring keeps the last min(S, capacity) of them). B <= 128, and the key
+ * rows of one (sequence, KV head) -- a linear cache's capacity, or
+ * window - 1 + S for a ring -- must not exceed 2^23; larger calls return
+ * HATTN_ERR_UNSUPPORTED. */
 int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k,
                   const void* v, const void* gate, int32_t batch,
                   int32_t seq_len, const int32_t* start_pos,

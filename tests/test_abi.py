@@ -90,6 +90,9 @@ def test_prefill_rejects_bad_arguments(L):
     cases.append((fu, hb.KvCacheC(0, FAKE, hb.KV_LINEAR, 1, 64), {}, -1))
     cases.append((fu, lin, {"B": 0, "start": (0,)}, -2))
     cases.append((fu, hb.KvCacheC(FAKE, FAKE, hb.KV_LINEAR, 200, 64), {"B": 200, "start": (0,) * 200}, -3))
+    big = hb.KvCacheC(FAKE, FAKE, hb.KV_LINEAR, 1, (1 << 23) + 1)
+    cases.append((fu, big, {}, -3))                                                    # 32-bit row offsets
+    cases.append((sl, ring, {"S": (1 << 23) - 510}, -3))                                 # 511 + S rows
     for desc, cache, kw, want in cases:
         got = _prefill(L, desc, cache, **kw)
         assert got == want, (desc.layer_type, kw, got, want)
