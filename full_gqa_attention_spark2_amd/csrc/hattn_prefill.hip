@@ -45,9 +45,31 @@ __device__ __forceinline__ s16x4 lds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
-// 16 bytes per lane from global memory to LDS; lane l lands at lds + 16*l.
-__device__ __forceinline__ void load_lds16(const void* g, char* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
+// Buffer resource over one (sequence, KV head) slab of key rows (raw
+// buffer, byte offsets, bounds = the slab size).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from the slab at byte offset voff + soff into LDS;
+// lane l lands at lds + 16*l. (A buffer load rather than a global one: the
+// compiler can then count LDS reads precisely around it instead of draining
+// them.)
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds, 16, voff, soff, 0, 0);
+}
+
+// Max and sum of a value over the lane pair (l, l ^ 32), by a VALU lane
+// swap (no LDS traffic). After the swap of x with itself, lanes below 32
+// hold (x[l], x[l + 32]) and the others (x[l - 32], x[l]): the pair in the
+// same order on both lanes.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -61,17 +83,55 @@ __device__ __forceinline__ void unpack8(uint4 u, float* x) {
   }
 }
 
+// Matrix-core streams of one tile step (see mma_stream in the kernel).
+constexpr int kStreamS = 0;    // S^T only (first tile)
+constexpr int kStreamSPv = 1;  // S^T of tile t+1 interleaved with P.V of tile t-1
+constexpr int kStreamPv = 2;   // P.V only (last tile)
+constexpr int stream_length(int mode) { return mode == kStreamSPv ? 64 : 32; }
+constexpr int stream_ahead(int mode) { return mode == kStreamSPv ? 6 : 3; }
+constexpr int stream_reads(int mode, int e) {  // LDS reads feeding element e
+  return mode == kStreamS ? 1 : mode == kStreamPv ? 2 : ((e & 1) ? 2 : 1);
+}
+
+// Scheduling-group barriers for one stream, in issue order: the reads of
+// the first `ahead` elements, then per element one MFMA, the reads of
+// element e + ahead and up to kValu VALU / transcendental instructions (the
+// softmax that runs beside the stream). Barriers only constrain the
+// instructions that precede them in the same basic block.
+constexpr int kSoftmaxValuPerMfma = 3;
+constexpr int kSgMfma = 0x008, kSgDsRead = 0x100, kSgValu = 0x002 | 0x400;
+template <int Mode, int E, int Valu>
+__device__ __forceinline__ void issue_order_tail() {
+  if constexpr (E < stream_length(Mode)) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    if constexpr (E + stream_ahead(Mode) < stream_length(Mode))
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, stream_reads(Mode, E + stream_ahead(Mode)), 0);
+    if constexpr (Valu > 0) __builtin_amdgcn_sched_group_barrier(kSgValu, Valu, 0);
+    issue_order_tail<Mode, E + 1, Valu>();
+  }
+}
+template <int Mode, int E, int Acc>
+struct StreamHead {
+  static constexpr int value = StreamHead<Mode, E - 1, Acc + stream_reads(Mode, E - 1)>::value;
+};
+template <int Mode, int Acc>
+struct StreamHead<Mode, 0, Acc> {
+  static constexpr int value = Acc;
+};
+template <int Mode, int Valu>
+__device__ __forceinline__ void issue_order() {
+  __builtin_amdgcn_sched_group_barrier(kSgDsRead, StreamHead<Mode, stream_ahead(Mode), 0>::value, 0);
+  issue_order_tail<Mode, 0, Valu>();
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a) {
-  // K slot layout: block (ks, h) = channels (2*ks + h)*8 .. +7 of the 64 rows,
-  // 16 B per row, at (2*ks + h) * 1 KiB. V slot layout: block (tt, db) at
-  // (tt*8 + db) * 1 KiB holds keys 16*tt .. +15 x channels 32*db .. +31 as 64
-  // units of 8 B; unit L = 16g + 4v + a of half j2 (512 B each) is key
-  // 16tt + 8j2 + 4(g/2) + v, channels 32db + 16(g%2) + 4a .. +3.
-  // Four separate arrays (not one indexed array) so the compiler can tell the
-  // slot being filled from the slot being read and does not wait for the
-  // in-flight tile loads before reading the current tile.
+  // Two K and two V tile slots (the swizzled block layout is described at
+  // load_tile below). Four separate arrays (not one indexed array) so the
+  // compiler can tell the slot being filled from the slot being read and
+  // does not wait for the in-flight tile loads before reading the current
+  // tile.
   __shared__ __attribute__((aligned(1024))) char k_lds0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char k_lds1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char v_lds0[kTileBytes];
@@ -100,26 +160,34 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   const int nt = (row_hi + kBN - 1) / kBN - t_lo;
 
   const size_t kv_off = ((size_t)b * a.Hkv + kvh) * (size_t)a.rows * kHeadDim;
-  const char* kbase = (const char*)(a.kc + kv_off);
-  const char* vbase = (const char*)(a.vc + kv_off);
+  // the host limits a slab to 2^23 rows of 512 B
+  const uint32_t slab_bytes = (uint32_t)min((uint64_t)a.rows * 512u, (uint64_t)0xffffffffu);
+  const __amdgpu_buffer_rsrc_t krs = slab_rsrc(a.kc + kv_off, slab_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = slab_rsrc(a.vc + kv_off, slab_bytes);
 
-  // Each wave stages 8 of the 32 K blocks and 8 of the 32 V blocks of a
-  // tile. Rows past the valid keys re-read the last valid key; their scores
-  // are masked, so they contribute exactly zero.
-  const int v_lane_key = 8 * (lane >> 5) + 4 * ((lane >> 4) & 1) + ((lane >> 1) & 3);
-  const int v_lane_col = 32 * ((lane >> 3) & 1) + 16 * (lane & 1);  // bytes
-  auto load_k = [&](int t, char* slot) __attribute__((always_inline)) {
+  // A K or V tile (64 key rows x 512 B) sits in LDS as 32 blocks of 1 KiB;
+  // block 4g + c holds rows 8g .. 8g+7, bytes 128c .. 128c+127 of each row.
+  // Inside a block, the 16-byte chunk k of row r is at position
+  // 8r + (k ^ sigma(g, r)), with sigma = r ^ (g & 1) for K and (2r) & 7 for
+  // V. Each load instruction fills one block from 8 whole 128-byte lines
+  // (one row segment per 8 lanes), and the swizzle keeps the MFMA fragment
+  // reads below free of bank conflicts. Each wave loads blocks 8w .. 8w+7.
+  // Rows past the valid keys re-read the last valid key; their scores are
+  // masked, so they contribute exactly zero.
+  const uint32_t k_chunk0 = 16u * ((lane & 7) ^ (lane >> 3));
+  const uint32_t k_chunk1 = 16u * ((lane & 7) ^ (lane >> 3) ^ 1);
+  const uint32_t v_chunk = 16u * ((lane & 7) ^ ((2 * (lane >> 3)) & 7));
+  auto load_tile = [&](__amdgpu_buffer_rsrc_t rs, uint32_t chunk0, uint32_t chunk1, int t, char* slot)
+      __attribute__((always_inline)) {
     char* dst = slot + wave * 8 * 1024;
-    const uint32_t off = (uint32_t)min(t * kBN + lane, nk - 1) * 512u + (uint32_t)wave * 128u;
+    const int row0 = t * kBN + 16 * wave + (lane >> 3);
+    const uint32_t off0 = (uint32_t)min(row0, nk - 1) * 512u + chunk0;
+    const uint32_t off1 = (uint32_t)min(row0 + 8, nk - 1) * 512u + chunk1;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) load_lds16(kbase + off + u * 16, dst + u * 1024);
+    for (int u = 0; u < 8; ++u) load_lds16(rs, u < 4 ? off0 : off1, 128 * (u & 3), dst + u * 1024);
   };
-  auto load_v = [&](int t, char* slot) __attribute__((always_inline)) {
-    char* dst = slot + wave * 8 * 1024;
-    const uint32_t off = (uint32_t)min(t * kBN + 16 * wave + v_lane_key, nk - 1) * 512u + (uint32_t)v_lane_col;
-#pragma unroll
-    for (int db = 0; db < 8; ++db) load_lds16(vbase + off + db * 64, dst + db * 1024);
-  };
+  auto load_k = [&](int t, char* slot) __attribute__((always_inline)) { load_tile(krs, k_chunk0, k_chunk1, t, slot); };
+  auto load_v = [&](int t, char* slot) __attribute__((always_inline)) { load_tile(vrs, v_chunk, v_chunk, t, slot); };
 
   // Start the first tiles moving before the query prologue.
   load_k(t_lo, k_lds0);
@@ -176,36 +244,27 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   float m_i = -1e30f;  // running max (log2 units) of this lane's query
   float l_i = 0.f;     // running sum
 
-  // V^T fragments: lane (16g + i) of a transposed read gets channel
-  // 32db + 16(g%2) + i of keys 16tt + 8j2 + 4(g/2) + 0..3, which are the key
-  // slots (g/2)*8 + 4*j2 + 0..3 of the P^T fragment.
-  const int tr_off = lane * 8;
-  // P.V with the V^T fragments read 3 MFMAs ahead of their use, so LDS
-  // latency hides behind the matrix cores.
-  auto pv = [&](const char* vslot, const bf16x8* p) __attribute__((always_inline)) {
-    const char* vt = vslot + tr_off;
-    constexpr int kAhead = 3;
-    s16x4 vl[kAhead + 1], vh[kAhead + 1];
+  // K fragment of S MFMA (k-step ks, key block h): lane l reads row
+  // 32h + l%32, channels 16ks + 8(l/32) .. +7, at
+  // k_addr[ks % 4] + 16384h + 1024(ks / 4).
+  int k_addr[4];
 #pragma unroll
-    for (int i = 0; i < kAhead; ++i) {
-      vl[i] = lds_read_tr(vt + i * 1024);
-      vh[i] = lds_read_tr(vt + i * 1024 + 512);
-    }
+  for (int q = 0; q < 4; ++q)
+    k_addr[q] = ((lane & 31) >> 3) * 4096 + 128 * (lane & 7) +
+                16 * ((2 * q + (lane >> 5)) ^ (lane & 7) ^ (((lane & 31) >> 3) & 1));
+  // V^T fragments by transposed reads: in 16-lane group G, source lane
+  // w + 4v fetches 8 B (channels 32db + 16(G%2) + 4w .. +3) of key
+  // 16tt + 8j2 + 4(G/2) + v; output lane i then holds channel
+  // 32db + 16(G%2) + i of those 4 keys, which are the key slots
+  // 8(G/2) + 4j2 + 0..3 of the P^T fragment. Address:
+  // v_addr[db % 2] + 8192tt + 4096j2 + 1024(db / 2).
+  int v_addr[2];
+  {
+    const int G = lane >> 4, w = lane & 3, v = (lane >> 2) & 3;
 #pragma unroll
-    for (int n = 0; n < 32; ++n) {  // n = tt*8 + db
-      if (n + kAhead < 32) {
-        vl[(n + kAhead) % (kAhead + 1)] = lds_read_tr(vt + (n + kAhead) * 1024);
-        vh[(n + kAhead) % (kAhead + 1)] = lds_read_tr(vt + (n + kAhead) * 1024 + 512);
-      }
-      const s16x8 both = __builtin_shufflevector(vl[n % (kAhead + 1)], vh[n % (kAhead + 1)], 0, 1, 2, 3, 4, 5, 6, 7);
-      acc[n & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), p[n >> 3], acc[n & 7], 0, 0, 0);
-    }
-    // Keep O resident in the accumulation registers between tiles (the
-    // register allocator otherwise parks it in VGPRs and copies it every
-    // tile).
-#pragma unroll
-    for (int db = 0; db < 8; ++db) asm volatile("" : "+a"(acc[db]));
-  };
+    for (int e = 0; e < 2; ++e)
+      v_addr[e] = 512 * (G >> 1) + 128 * v + 16 * ((4 * e + 2 * (G & 1) + (w >> 1)) ^ (2 * v)) + 8 * (w & 1);
+  }
 
   // Mask of tile t's scores. Register i of block kb holds key row
   // t*64 + kb*32 + 8*(i/4) + 4*(lane/32) + i%4 for query lane % 32.
@@ -220,42 +279,70 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
       s1[i] = ok1 ? s1[i] : -__builtin_inff();
     }
   };
-  // S^T with the K fragments read 3 k-steps ahead of their use.
-  auto compute_s = [&](const char* kslot, f32x16& s0, f32x16& s1) __attribute__((always_inline)) {
-    const char* base = kslot + (lane >> 5) * 1024 + (lane & 31) * 16;
-    constexpr int kAhead = 3;
-    bf16x8 fa[kAhead + 1], fb[kAhead + 1];
-#pragma unroll
-    for (int i = 0; i < kAhead; ++i) {
-      fa[i] = *(const bf16x8*)(base + i * 2048);
-      fb[i] = *(const bf16x8*)(base + i * 2048 + 512);
-    }
-    s0 = f32x16{};
-    s1 = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      if (ks + kAhead < 16) {
-        fa[(ks + kAhead) % (kAhead + 1)] = *(const bf16x8*)(base + (ks + kAhead) * 2048);
-        fb[(ks + kAhead) % (kAhead + 1)] = *(const bf16x8*)(base + (ks + kAhead) * 2048 + 512);
+
+  // One stream of matrix-core work per tile: S^T of the next tile (32
+  // MFMAs, K fragments from LDS) interleaved with P.V of the previous tile
+  // (32 MFMAs, V^T fragments from LDS). With both, stream element e is an S
+  // MFMA when e is even and a P.V MFMA when odd. The LDS fragments of
+  // element e + ahead are read just before element e issues; the
+  // scheduling-group barriers placed after the step's code (issue_order)
+  // hold the compiler to that order, so every read has several MFMAs to land.
+  auto mma_stream = [&](auto mode, const char* kslot, const char* vslot, f32x16& s0, f32x16& s1,
+                        const bf16x8* p) __attribute__((always_inline)) {
+    constexpr bool kS = decltype(mode)::value != kStreamPv;
+    constexpr bool kP = decltype(mode)::value != kStreamS;
+    constexpr int kN = stream_length(decltype(mode)::value);
+    constexpr int kAhead = stream_ahead(decltype(mode)::value);
+    bf16x8 kr[4];
+    s16x8 vr[4];
+    auto is_s = [](int e) { return kS && (!kP || (e & 1) == 0); };
+    auto index = [](int e) { return (kS && kP) ? e >> 1 : e; };
+    auto issue = [&](int e) __attribute__((always_inline)) {
+      const int i = index(e);
+      if (is_s(e)) {  // S MFMA i: k-step i/2, key block i%2
+        const int ks = i >> 1;
+        kr[i & 3] = *(const bf16x8*)(kslot + k_addr[ks & 3] + (i & 1) * 16384 + (ks >> 2) * 1024);
+      } else {        // P.V MFMA i = tt*8 + db
+        const char* vp = vslot + v_addr[i & 1] + (i >> 3) * 8192 + ((i & 7) >> 1) * 1024;
+        const s16x4 lo = lds_read_tr(vp);
+        const s16x4 hi = lds_read_tr(vp + 4096);
+        vr[i & 3] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks % (kAhead + 1)], qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks % (kAhead + 1)], qf[ks], s1, 0, 0, 0);
+    };
+    if (kS) {
+      s0 = f32x16{};
+      s1 = f32x16{};
     }
-    // scores feed VALU code: produce them in VGPRs
-    asm volatile("" : "+v"(s0), "+v"(s1));
+#pragma unroll
+    for (int e = 0; e < kAhead; ++e) issue(e);
+#pragma unroll
+    for (int e = 0; e < kN; ++e) {
+      if (e + kAhead < kN) issue(e + kAhead);
+      const int i = index(e);
+      if (is_s(e)) {
+        if (i & 1)
+          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[i & 3], qf[i >> 1], s1, 0, 0, 0);
+        else
+          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[i & 3], qf[i >> 1], s0, 0, 0, 0);
+      } else {
+        acc[i & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vr[i & 3]), p[i >> 3],
+                                                            acc[i & 7], 0, 0, 0);
+      }
+    }
   };
+
   // Softmax of one tile's scores into pb. The running max moves only when
   // the tile's max exceeds it by more than 2^8; returns the factor O must be
   // rescaled by (1 when the max did not move).
-  auto softmax = [&](f32x16& s0, f32x16& s1, bf16x8* pb) __attribute__((always_inline)) {
+  auto softmax = [&](f32x16& s0, f32x16& s1, bf16x8* pb, float& alpha) __attribute__((always_inline)) {
     float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-    mx = fmaxf(mx, wave_shfl_xor(mx, 32)) * kScoreScale;
+    mx = pair_max(mx) * kScoreScale;
     const float m_new = fmaxf(m_i, mx);
     const bool rescale = __any(m_new > m_i + kRescaleSlack);
     const float m_use = rescale ? m_new : m_i;
-    const float alpha = fast_exp2(m_i - m_use);
+    alpha = fast_exp2(m_i - m_use);
     // step tt of P^T covers keys 16tt .. +15; its key slot (lane/32)*8 + j
     // is register 8*(tt%2) + j of block tt/2
     float rs = 0.f;
@@ -267,28 +354,25 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
       pb[i >> 3][i & 7] = (__bf16)p0;
       pb[2 + (i >> 3)][i & 7] = (__bf16)p1;
     }
-    rs += wave_shfl_xor(rs, 32);
-    l_i = l_i * alpha + rs;
+    l_i = l_i * alpha + rs;   // per-lane partial; the lane pair is summed at the end
     m_i = m_use;
-    return rescale ? alpha : 1.0f;
+    return rescale;
   };
   // O *= alpha in place in the accumulation registers (read, multiply,
   // write back per element), so O never has to move to VGPRs.
   auto rescale_o = [&](float alpha) __attribute__((always_inline)) {
-    if (alpha != 1.0f) {
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
+    for (int db = 0; db < 8; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float tmp;
-          asm volatile(
-              "v_accvgpr_read_b32 %1, %0\n\t"
-              "v_mul_f32 %1, %1, %2\n\t"
-              "v_accvgpr_write_b32 %0, %1"
-              : "+a"(acc[db][i]), "=&v"(tmp)
-              : "v"(alpha));
-        }
-    }
+      for (int i = 0; i < 16; ++i) {
+        float tmp;
+        asm volatile(
+            "v_accvgpr_read_b32 %1, %0\n\t"
+            "v_mul_f32 %1, %1, %2\n\t"
+            "v_accvgpr_write_b32 %0, %1"
+            : "+a"(acc[db][i]), "=&v"(tmp)
+            : "v"(alpha));
+      }
   };
 
   // Iteration j (tile t = t_lo + j) overlaps three things: the softmax of
@@ -296,46 +380,61 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   // of K(t+2) and V(t). Tile j's K lives in k_lds[j % 2] and its V in
   // v_lds[j % 2]; the score and probability registers alternate the same
   // way, so every slot and register set is fixed at compile time.
+  using ModeS = std::integral_constant<int, kStreamS>;
+  using ModeSPv = std::integral_constant<int, kStreamSPv>;
+  using ModePv = std::integral_constant<int, kStreamPv>;
   load_k(t_lo, k_lds0);
   if (nt > 1) load_k(t_lo + 1, k_lds1);
+  bool rescale_pending = false;
+  float alpha_pending = 1.0f;
   f32x16 sA0, sA1, sB0, sB1;  // scores of even / odd tiles
   bf16x8 pA[4], pB[4];        // probabilities of even / odd tiles
   wait_loads();
   __syncthreads();
-  compute_s(k_lds0, sA0, sA1);
+  mma_stream(ModeS{}, k_lds0, v_lds0, sA0, sA1, pA);
+  issue_order<kStreamS, 0>();
   if (need_mask(t_lo)) mask_s(t_lo, sA0, sA1);
 
-  // One iteration; kPv is false only for the first tile. On the last tile
-  // S(t+1) is computed from a stale slot and discarded, which keeps the body
-  // free of branches between its MFMAs and its softmax.
-  auto step = [&](auto has_pv, int j, const char* kn, const char* vp, char* kf, char* vf, f32x16& sc0,
+  // One iteration; the first one has no P.V yet. On the last tile S(t+1)
+  // is computed from a stale slot and discarded, which keeps the body free
+  // of branches between its MFMAs and its softmax.
+  auto step = [&](auto mode, int j, const char* kn, const char* vp, char* kf, char* vf, f32x16& sc0,
                   f32x16& sc1, f32x16& sn0, f32x16& sn1, const bf16x8* pp,
                   bf16x8* pn) __attribute__((always_inline)) {
-    constexpr bool kPv = decltype(has_pv)::value;
+    constexpr int kMode = decltype(mode)::value;
     const int t = t_lo + j;
     wait_loads();
     __syncthreads();
     if (j + 2 < nt) load_k(t + 2, kf);
     load_v(t, vf);
-    compute_s(kn, sn0, sn1);
-    if (kPv) pv(vp, pp);
-    const float alpha = softmax(sc0, sc1, pn);
-    rescale_o(alpha);
+    // O holds P.V up to tile t-2 plus (below) tile t-1, all relative to the
+    // max before softmax(t-1); a max move found by softmax(t-1) is applied
+    // here, before P(t-1).V(t-1) is added, keeping the stream and the
+    // softmax in one branch-free block.
+    if (rescale_pending) rescale_o(alpha_pending);
+    mma_stream(mode, kn, vp, sn0, sn1, pp);
+    rescale_pending = softmax(sc0, sc1, pn, alpha_pending);
+    issue_order<kMode, kSoftmaxValuPerMfma>();
     if (j + 1 < nt && need_mask(t + 1)) mask_s(t + 1, sn0, sn1);
   };
-  using T_ = std::integral_constant<bool, true>;
-  using F_ = std::integral_constant<bool, false>;
   // even j: S(t) in sA, P(t) -> pA, P(t-1) in pB; odd j: the other way round
-  step(F_{}, 0, k_lds1, v_lds1, k_lds0, v_lds0, sA0, sA1, sB0, sB1, pB, pA);
+  step(ModeS{}, 0, k_lds1, v_lds1, k_lds0, v_lds0, sA0, sA1, sB0, sB1, pB, pA);
   for (int j = 1; j < nt; j += 2) {
-    step(T_{}, j, k_lds0, v_lds0, k_lds1, v_lds1, sB0, sB1, sA0, sA1, pA, pB);
-    if (j + 1 < nt) step(T_{}, j + 1, k_lds1, v_lds1, k_lds0, v_lds0, sA0, sA1, sB0, sB1, pB, pA);
+    step(ModeSPv{}, j, k_lds0, v_lds0, k_lds1, v_lds1, sB0, sB1, sA0, sA1, pA, pB);
+    if (j + 1 < nt) step(ModeSPv{}, j + 1, k_lds1, v_lds1, k_lds0, v_lds0, sA0, sA1, sB0, sB1, pB, pA);
   }
   // P.V of the last tile
   wait_loads();
   __syncthreads();
-  if ((nt - 1) & 1) pv(v_lds1, pB);
-  else pv(v_lds0, pA);
+  if (rescale_pending) rescale_o(alpha_pending);
+  if ((nt - 1) & 1) {
+    mma_stream(ModePv{}, k_lds0, v_lds1, sA0, sA1, pB);
+    issue_order<kStreamPv, 0>();
+  } else {
+    mma_stream(ModePv{}, k_lds0, v_lds0, sA0, sA1, pA);
+    issue_order<kStreamPv, 0>();
+  }
+  l_i = pair_sum(l_i);
 
   // ---- epilogue: divide by the softmax sum, gate in fp32, one bf16 store.
   // acc[db] register i holds channel db*32 + 8*(i/4) + 4*(lane/32) + i%4.
