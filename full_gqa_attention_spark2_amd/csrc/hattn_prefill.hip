@@ -88,6 +88,8 @@ constexpr int kStreamS = 0;    // S^T only (first tile)
 constexpr int kStreamSPv = 1;  // S^T of tile t+1 interleaved with P.V of tile t-1
 constexpr int kStreamPv = 2;   // P.V only (last tile)
 constexpr int stream_length(int mode) { return mode == kStreamSPv ? 64 : 32; }
+constexpr int kRing = 4;  // fragment registers per operand kind
+// LDS reads run this many stream elements ahead of their MFMA
 constexpr int stream_ahead(int mode) { return mode == kStreamSPv ? 6 : 3; }
 constexpr int stream_reads(int mode, int e) {  // LDS reads feeding element e
   return mode == kStreamS ? 1 : mode == kStreamPv ? 2 : ((e & 1) ? 2 : 1);
@@ -293,20 +295,20 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
     constexpr bool kP = decltype(mode)::value != kStreamS;
     constexpr int kN = stream_length(decltype(mode)::value);
     constexpr int kAhead = stream_ahead(decltype(mode)::value);
-    bf16x8 kr[4];
-    s16x8 vr[4];
+    bf16x8 kr[kRing];
+    s16x8 vr[kRing];
     auto is_s = [](int e) { return kS && (!kP || (e & 1) == 0); };
     auto index = [](int e) { return (kS && kP) ? e >> 1 : e; };
     auto issue = [&](int e) __attribute__((always_inline)) {
       const int i = index(e);
       if (is_s(e)) {  // S MFMA i: k-step i/2, key block i%2
         const int ks = i >> 1;
-        kr[i & 3] = *(const bf16x8*)(kslot + k_addr[ks & 3] + (i & 1) * 16384 + (ks >> 2) * 1024);
+        kr[i % kRing] = *(const bf16x8*)(kslot + k_addr[ks & 3] + (i & 1) * 16384 + (ks >> 2) * 1024);
       } else {        // P.V MFMA i = tt*8 + db
         const char* vp = vslot + v_addr[i & 1] + (i >> 3) * 8192 + ((i & 7) >> 1) * 1024;
         const s16x4 lo = lds_read_tr(vp);
         const s16x4 hi = lds_read_tr(vp + 4096);
-        vr[i & 3] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        vr[i % kRing] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
     };
     if (kS) {
@@ -321,11 +323,11 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
       const int i = index(e);
       if (is_s(e)) {
         if (i & 1)
-          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[i & 3], qf[i >> 1], s1, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[i % kRing], qf[i >> 1], s1, 0, 0, 0);
         else
-          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[i & 3], qf[i >> 1], s0, 0, 0, 0);
+          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[i % kRing], qf[i >> 1], s0, 0, 0, 0);
       } else {
-        acc[i & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vr[i & 3]), p[i >> 3],
+        acc[i & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vr[i % kRing]), p[i >> 3],
                                                             acc[i & 7], 0, 0, 0);
       }
     }
@@ -335,26 +337,36 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   // the tile's max exceeds it by more than 2^8; returns the factor O must be
   // rescaled by (1 when the max did not move).
   auto softmax = [&](f32x16& s0, f32x16& s1, bf16x8* pb, float& alpha) __attribute__((always_inline)) {
-    float mx = fmaxf(s0[0], s1[0]);
+    // reductions as balanced trees: short dependency chains interleave
+    // with the matrix-core stream without stalling it
+    float t16[16];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-    mx = pair_max(mx) * kScoreScale;
+    for (int i = 0; i < 16; ++i) t16[i] = fmaxf(s0[i], s1[i]);
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+      for (int i = 0; i < w; ++i) t16[i] = fmaxf(t16[i], t16[i + w]);
+    const float mx = pair_max(t16[0]) * kScoreScale;
     const float m_new = fmaxf(m_i, mx);
     const bool rescale = __any(m_new > m_i + kRescaleSlack);
     const float m_use = rescale ? m_new : m_i;
     alpha = fast_exp2(m_i - m_use);
     // step tt of P^T covers keys 16tt .. +15; its key slot (lane/32)*8 + j
     // is register 8*(tt%2) + j of block tt/2
-    float rs = 0.f;
+    float q16[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float p0 = fast_exp2(fmaf(s0[i], kScoreScale, -m_use));
       const float p1 = fast_exp2(fmaf(s1[i], kScoreScale, -m_use));
-      rs += p0 + p1;
+      q16[i] = p0 + p1;
       pb[i >> 3][i & 7] = (__bf16)p0;
       pb[2 + (i >> 3)][i & 7] = (__bf16)p1;
     }
-    l_i = l_i * alpha + rs;   // per-lane partial; the lane pair is summed at the end
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+      for (int i = 0; i < w; ++i) q16[i] += q16[i + w];
+    l_i = l_i * alpha + q16[0];   // per-lane partial; the lane pair is summed at the end
     m_i = m_use;
     return rescale;
   };
