@@ -42,11 +42,12 @@ __device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + expf
 
 }  // namespace
 
-__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) char vbuf[4][kChunk * kVPitch];   // 68 KiB
+template <int kWaves>
+__global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void decode_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) char vbuf[kWaves][kChunk * kVPitch];   // 17 KiB per wave
   __shared__ __attribute__((aligned(16))) uint16_t qcols[8][kHeadDim];  // 4 KiB
-  __shared__ float red_m[4][4];
-  __shared__ float red_l[4][4];
+  __shared__ float red_m[kWaves][4];
+  __shared__ float red_l[kWaves][4];
 
   const int sp = (int)blockIdx.x % a.nsplit;
   const int r2 = (int)blockIdx.x / a.nsplit;
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 
   const int p = a.pos[b];
   if (p < 0 || p > a.max_pos) {
-    if (a.nsplit == 1) {
+    if (a.nsplit == 1 && t < kHeadDim) {
       for (int hh = 0; hh < kGroup; ++hh)
         a.out[((size_t)b * a.Hq + kvh * kGroup + hh) * kHeadDim + t] = 0x7fc0;  // NaN
     }
@@ -71,29 +72,40 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   const int slot = cache_slot(p, a.ring, a.cap);
   const size_t kv_off = ((size_t)b * a.Hkv + kvh) * (size_t)a.cap * kHeadDim;
 
-  // ---- RoPE of the 4 queries (fp64 angle and rotation), split into bf16
-  // high and low parts; the owner of the new slot also writes the new key.
-  {
+  // ---- RoPE of the 4 queries: cos/sin of the fp64-reduced angle, rotation
+  // in fp32, split into bf16 high and low parts (~16 significant bits, far
+  // above what the scores need). The owner of the new slot also writes the
+  // new key, rotated in fp64 and rounded once to bf16 like every cached key.
+  if (t < kHeadDim) {
     const int d = t;
     const int half = a.r >> 1;
     double c = 1.0, s = 0.0;
     if (d < a.r) rope_sincos(p, a.inv_freq[d < half ? d : d - half], &s, &c);
-    auto rot = [&](const uint16_t* x) -> double {
-      const double xd = (double)bf16_bits_to_float(x[d]);
+    const float cf = (float)c, sf = (float)s;
+    const int dp = d < half ? d + half : d - half;  // rotation partner
+    auto rot32 = [&](const uint16_t* x) -> float {
+      const float xd = bf16_bits_to_float(x[d]);
       if (d >= a.r) return xd;
-      if (d < half) return xd * c - (double)bf16_bits_to_float(x[d + half]) * s;
-      return xd * c + (double)bf16_bits_to_float(x[d - half]) * s;
+      const float xp = bf16_bits_to_float(x[dp]);
+      return d < half ? fmaf(xd, cf, -xp * sf) : fmaf(xd, cf, xp * sf);
     };
 #pragma unroll
     for (int hh = 0; hh < kGroup; ++hh) {
-      const double y = rot(a.q + ((size_t)b * a.Hq + kvh * kGroup + hh) * kHeadDim);
-      const uint16_t yh = double_to_bf16_bits(y);
+      const float y = rot32(a.q + ((size_t)b * a.Hq + kvh * kGroup + hh) * kHeadDim);
+      const uint16_t yh = float_to_bf16_bits(y);
       qcols[hh][d] = yh;
-      qcols[4 + hh][d] = double_to_bf16_bits(y - (double)bf16_bits_to_float(yh));
+      qcols[4 + hh][d] = float_to_bf16_bits(y - bf16_bits_to_float(yh));
     }
     if (slot >= k0 && slot < k1) {
       const size_t nk_off = ((size_t)b * a.Hkv + kvh) * kHeadDim;
-      a.kc[kv_off + (size_t)slot * kHeadDim + d] = double_to_bf16_bits(rot(a.k + nk_off));
+      const uint16_t* x = a.k + nk_off;
+      const double xd = (double)bf16_bits_to_float(x[d]);
+      double y = xd;
+      if (d < a.r) {
+        const double xp = (double)bf16_bits_to_float(x[dp]);
+        y = d < half ? xd * c - xp * s : xd * c + xp * s;
+      }
+      a.kc[kv_off + (size_t)slot * kHeadDim + d] = double_to_bf16_bits(y);
       a.vc[kv_off + (size_t)slot * kHeadDim + d] = a.v[nk_off + d];
     }
   }
@@ -122,7 +134,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 
   const int tr_a = col & 3, tr_v = col >> 2;
   const int nchunks = k1 > k0 ? (k1 - k0 + kChunk - 1) / kChunk : 0;
-  for (int c = wave; c < nchunks; c += 4) {
+  for (int c = wave; c < nchunks; c += kWaves) {
     const int ck = k0 + c * kChunk;
     // K fragments: lane holds key ck + kb*16 + col, channels ks*32 + grp*8 ..
     // Keys past the split end re-read its last key and are masked below.
@@ -225,7 +237,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
-  // ---- merge high and low rows (groups 0 and 1), then the 4 waves.
+  // ---- merge high and low rows (groups 0 and 1), then the waves.
 #pragma unroll
   for (int blk = 0; blk < 16; ++blk)
 #pragma unroll
@@ -243,15 +255,16 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     red_l[wave][lane] = l_run;
   }
   __syncthreads();
+  if (t >= kHeadDim) return;
   const int d = t;
 #pragma unroll
   for (int hh = 0; hh < kGroup; ++hh) {
     float M = red_m[0][hh];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, red_m[w][hh]);
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, red_m[w][hh]);
     float L = 0.f, O = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kWaves; ++w) {
       const float e = fast_exp2(red_m[w][hh] - M);
       L += e * red_l[w][hh];
       O += e * om[(w * 4 + hh) * kHeadDim + d];
@@ -338,7 +351,10 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const int grid = a.B * a.Hkv * a.nsplit;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_kernel, dim3(grid), dim3(256), 0, s, a);
+  if (a.waves == 8)
+    hipLaunchKernelGGL(decode_kernel<8>, dim3(grid), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL(decode_kernel<4>, dim3(grid), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(a.B * a.Hq), dim3(kMergeThreads), 0, s, a);

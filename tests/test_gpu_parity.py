@@ -340,6 +340,37 @@ def test_decode_out_of_range_position_gives_nan_and_no_write():
     assert not cache.k[1].any() and cache.k[0, :, 5].any()
 
 
+def test_decode_wide_grid_partial_rings_and_invalid_positions():
+    # 64 sequences x 4 KV heads reach the one-workgroup-per-pair decode grid;
+    # mix partial rings, full rings and positions outside [0, max_pos]
+    B = 64
+    rng = np.random.default_rng(11)
+    pos = rng.integers(0, 5000, B).astype(np.int64)
+    pos[:8] = [0, 1, 17, 255, 510, 511, 512, 4999]
+    pos[20], pos[41] = -1, 6000  # invalid: negative, and above max_pos below
+    max_pos = 5000
+    desc = hb.layer_desc("sliding")
+    inp = synth.decode_inputs(B, 16, 4, seed=12)
+    ck = synth.cache_tensor(B, 4, 512, seed=800)
+    cv = synth.cache_tensor(B, 4, 512, seed=801)
+    cache = hb.KVCache(ck.to(DEV), cv.to(DEV), "ring")
+    d = to_dev(inp)
+    out = hb.hattn_decode(desc, d["q"], d["k"], d["v"], d["gate"], torch.as_tensor(pos, dtype=torch.int32).to(DEV),
+                          max_pos, cache)
+    torch.cuda.synchronize()
+    bad = np.array([20, 41])
+    good = np.setdiff1d(np.arange(B), bad)
+    assert torch.isnan(out[bad].float()).all()
+    assert torch.equal(cache.k[bad].cpu(), ck[bad]) and torch.equal(cache.v[bad].cpu(), cv[bad])
+    sub = {k: v[good] for k, v in inp.items()}
+    ref, slots, k_hat = O.decode_ref(sub["q"], sub["k"], sub["v"], sub["gate"], pos[good], ck[good], cv[good],
+                                     kind="ring", window=512, theta=desc.rope_theta,
+                                     rotary_fraction=desc.rotary_fraction)
+    check("decode wide grid (64 x 4 pairs), partial rings", out[good].cpu(), ref)
+    for i, b in enumerate(good[:8]):
+        check_bf16_values(f"decode key b={b}", cache.k[b, :, int(slots[i])].cpu(), k_hat[i])
+
+
 # ------------------------------------------------------------------ chunked prefill, 1.7B shape
 @pytest.mark.parametrize("layer", ["full", "sliding"])
 def test_chunked_prefill_1p7b_shape_sampled(layer):
