@@ -17,7 +17,7 @@ namespace {
 constexpr int kHeadDimSupported = 256;
 constexpr int kGroupSupported = 4;
 constexpr int kMaxPos = 1 << 30;
-constexpr int kDecodeTargetBlocks = 512;  // ~2 resident blocks per CU
+constexpr int kDecodeTargetBlocks = 1024;  // 4 rounds of one workgroup per CU
 constexpr long long kMaxDecodeSplits = 2048;  // the merge kernel's limit
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -136,27 +136,24 @@ long long decode_span(const hattn_layer_desc* d, const hattn_kv_cache* c, long l
 struct DecodePlan {
   int nsplit;
   int split_keys;
-  int waves;
 };
 
 // With at least this many (sequence, KV head) pairs, each pair gets one
-// 8-wave workgroup over its whole key range (one per CU, no split merge).
+// workgroup over its whole key range (one per CU, no split merge).
 constexpr long long kDecodeWidePairs = 256;
 
 // Otherwise split the key range so that the grid holds about
-// kDecodeTargetBlocks 4-wave workgroups, in multiples of 128 keys (one
-// 32-key chunk per wave).
+// kDecodeTargetBlocks workgroups, in multiples of 128 keys.
 DecodePlan decode_plan(const hattn_layer_desc* d, const hattn_kv_cache* c, int B, long long span) {
   const long long base = (long long)B * d->num_kv_heads;
-  if (base >= kDecodeWidePairs) return DecodePlan{1, (int)((span + 127) / 128 * 128), 8};
+  if (base >= kDecodeWidePairs) return DecodePlan{1, (int)((span + 127) / 128 * 128)};
   long long want = (kDecodeTargetBlocks + base - 1) / base;
   long long most = (span + 127) / 128;
   long long n = std::max<long long>(1, std::min({want, most, (long long)kMaxDecodeSplits}));
   long long keys = (span + n - 1) / n;
   keys = (keys + 127) / 128 * 128;
   n = (span + keys - 1) / keys;
-  DecodePlan p{(int)n, (int)keys, 4};
-  return p;
+  return DecodePlan{(int)n, (int)keys};
 }
 
 }  // namespace
@@ -409,7 +406,6 @@ int hattn_decode(const hattn_layer_desc* desc, const void* q, const void* k, con
   fill_inv_freq(desc->rope_theta, a.r, a.inv_freq);
   a.nsplit = p.nsplit;
   a.split_keys = p.split_keys;
-  a.waves = p.waves;
   hipEvent_t prof = profile_begin(HATTN_PROFILE_DECODE, stream);
   const hipError_t e = launch_decode(a, stream);
   profile_end(prof, stream);

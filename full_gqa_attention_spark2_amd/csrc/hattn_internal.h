@@ -73,7 +73,6 @@ struct DecodeArgs {
   int r;
   int nsplit;
   int split_keys;         // keys per split, multiple of 128
-  int waves;              // waves per workgroup: 4, or 8 for one workgroup per (sequence, KV head)
   double inv_freq[128];
 };
 
