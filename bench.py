@@ -10,6 +10,12 @@ gate: every stage of the prefill path). ``value`` is its algorithmic
 throughput in TFLOP/s: 4 * 256 * 16 * (visible query-key pairs) per call
 divided by the event-timed duration of the K timed calls.
 
+Two more prefill workloads are reported under "prefill_configs" (not in
+``value``): a sliding layer at 1024 tokens (batch 1, ring cache), and the
+1.7B shape's chunked prefill (8 / 2 heads, batch 2, a 4096-token chunk on a
+262144-token context), whose 28-layer time is composed from one timed call
+per layer type (21 sliding + 7 full layers).
+
 Decode is timed in its own section after the prefill steps and reported under
 "decode": sliding-layer decode over 64 sequences with 512-slot ring caches,
 and full-layer decode over 2^20 cached tokens (batch 1) and 8 x 131072
@@ -107,6 +113,22 @@ def time_calls(torch, fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def time_each(torch, fn, steps, warmup):
+    """Per-call event times (ms): median, p10, p90."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    pick = lambda f: t[min(len(t) - 1, int(f * (len(t) - 1) + 0.5))]
+    return {"median": pick(0.5), "p10": pick(0.1), "p90": pick(0.9)}
+
+
 def cpu_baseline(S=8192, budget_s=12.0):
     """The fp64 oracle on a bounded sample of the headline workload, on host
     cores: interleaved sets of 512 evenly spaced query rows (rows k, k+16,
@@ -170,9 +192,7 @@ def run(args):
     flops = 4 * 256 * Hq * visible_pairs(S, 0)
     hb.hattn_profile_read(hb.PROFILE_PREFILL)
     hb.hattn_profile_enable(True)
-    t_wall = time.perf_counter()
     ms = time_calls(torch, prefill, args.steps, args.warmup)
-    t_wall = time.perf_counter() - t_wall
     hb.hattn_profile_enable(False)
     n, attn_total = hb.hattn_profile_read(hb.PROFILE_PREFILL)
     attn_ms = attn_total / max(n, 1)
@@ -188,6 +208,55 @@ def run(args):
     }
     del inp, cache, out, ws
     torch.cuda.empty_cache()
+
+    # ------------------------------------------------ other prefill workloads
+    prefill_configs = None
+    if not args.skip_prefill_configs:
+        prefill_configs = {}
+
+        def prefill_case(layer, B, S_, Hq_, Hkv_, s0, cap, kind, fill, seed, steps, warmup):
+            d = hb.layer_desc(layer, Hq_, Hkv_)
+            pin = {k: v.to(dev) for k, v in synth.prefill_inputs(B, S_, Hq_, Hkv_, seed=seed).items()}
+            c = hb.KVCache(synth.cache_tensor(B, Hkv_, cap, seed=seed + 1, fill_tokens=fill, threads=16).to(dev),
+                           synth.cache_tensor(B, Hkv_, cap, seed=seed + 2, fill_tokens=fill, threads=16).to(dev),
+                           kind)
+            o = torch.empty_like(pin["q"])
+            w = torch.empty(max(hb.prefill_workspace_size(d, c, B, S_), 256), dtype=torch.uint8, device=dev)
+            starts = [s0] * B
+
+            def call():
+                hb.hattn_prefill(d, pin["q"], pin["k"], pin["v"], pin["gate"], starts, c, out=o, workspace=w)
+
+            t = time_each(torch, call, steps, warmup)
+            win = 512 if layer == "sliding" else None
+            fl = 4 * 256 * Hq_ * B * visible_pairs(S_, s0, window=win)
+            return t, fl
+
+        # sliding layer, batch 1, 1024 tokens from position 0 (empty ring)
+        t, fl = prefill_case("sliding", 1, 1024, Hq, Hkv, 0, 512, "ring", 0, 30, max(args.steps, 20), args.warmup)
+        tf = fl / (t["median"] * 1e-3) / 1e12
+        log(f"prefill sliding_s1024: {t['median'] * 1e3:.1f} us per call (median), {tf:.1f} TFLOP/s")
+        prefill_configs["sliding_s1024"] = {
+            "us_per_call": {k: round(v * 1e3, 2) for k, v in t.items()}, "flop_per_call": fl,
+            "TFLOP_per_s": round(tf, 2), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        # 1.7B shape: 8 / 2 heads, batch 2, a 4096-token chunk at 262144
+        s0, S5 = 262144, 4096
+        ts, fls = prefill_case("sliding", 2, S5, 8, 2, s0, 512, "ring", None, 40, 5, 2)
+        torch.cuda.empty_cache()
+        tfu, flf = prefill_case("full", 2, S5, 8, 2, s0, s0 + S5, "linear", s0, 50, 5, 2)
+        torch.cuda.empty_cache()
+        ms28 = 21 * ts["median"] + 7 * tfu["median"]
+        fl28 = 21 * fls + 7 * flf
+        tf28 = fl28 / (ms28 * 1e-3) / 1e12
+        log(f"prefill 1.7B chunk (28 layers): {ms28:.2f} ms, {tf28:.1f} TFLOP/s "
+            f"(sliding layer {ts['median']:.3f} ms, full layer {tfu['median']:.3f} ms)")
+        prefill_configs["chunked_1p7b_28_layers"] = {
+            "ms_28_layers": round(ms28, 3), "flop_28_layers": fl28, "TFLOP_per_s": round(tf28, 2),
+            "frac_bf16_peak": round(tf28 / PEAK_BF16_TFLOPS, 4),
+            "composed_from": "21 x sliding-layer call + 7 x full-layer call, medians",
+            "sliding_layer_ms": {k: round(v, 4) for k, v in ts.items()}, "sliding_layer_flop": fls,
+            "full_layer_ms": {k: round(v, 4) for k, v in tfu.items()}, "full_layer_flop": flf,
+            "full_layer_TFLOP_per_s": round(flf / (tfu["median"] * 1e-3) / 1e12, 2)}
 
     # ---------------------------------------------------------------- decode
     # Each decode workload is timed as K back-to-back calls (decode kernel and
@@ -267,6 +336,7 @@ def run(args):
         },
         "roofline": roofline,
         "decode": decode,
+        "prefill_configs": prefill_configs,
     }
     if not args.skip_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
@@ -279,6 +349,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--skip-prefill-configs", action="store_true",
+                    help="skip the sliding 1024-token and 1.7B chunked prefill timings")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the copy of known size used to scale HBM counters")
