@@ -201,6 +201,9 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   // ks*16 + (lane / 32)*8 .. +7 for ks = 0..15.
   const int qrow = q0 + (lane & 31);
   const bool qvalid = qrow < a.S;
+  // the gate logit, requested now and used in the epilogue
+  const size_t orow = ((size_t)b * a.S + (qvalid ? qrow : a.S - 1)) * a.Hq + h;
+  const uint16_t gate_bits = a.gate[orow];
   bf16x8 qf[16];
   {
     const int qr = qvalid ? qrow : a.S - 1;
@@ -395,8 +398,6 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   using ModeS = std::integral_constant<int, kStreamS>;
   using ModeSPv = std::integral_constant<int, kStreamSPv>;
   using ModePv = std::integral_constant<int, kStreamPv>;
-  load_k(t_lo, k_lds0);
-  if (nt > 1) load_k(t_lo + 1, k_lds1);
   bool rescale_pending = false;
   float alpha_pending = 1.0f;
   f32x16 sA0, sA1, sB0, sB1;  // scores of even / odd tiles
@@ -451,8 +452,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   // ---- epilogue: divide by the softmax sum, gate in fp32, one bf16 store.
   // acc[db] register i holds channel db*32 + 8*(i/4) + 4*(lane/32) + i%4.
   if (qvalid) {
-    const size_t orow = ((size_t)b * a.S + qrow) * a.Hq + h;
-    const float g = bf16_bits_to_float(a.gate[orow]);
+    const float g = bf16_bits_to_float(gate_bits);
     const float f = (1.0f / l_i) * (1.0f / (1.0f + expf(-g)));
     uint16_t* op = a.out + orow * kHeadDim + 4 * (lane >> 5);
 #pragma unroll
