@@ -257,14 +257,19 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   const int k_base = (col >> 1) * 1024 + (col & 1) * 512;
   const int v_base = kChunkBytes + (vr_row >> 1) * 1024 + (vr_row & 1) * 512 + 8 * (vr_w & 1);
 
-  // The new token's row in the LDS copy of its chunk (row slot - key0).
+  // The new token's rows in the LDS copy of its chunk: row slot - key0, and
+  // when the slot is the last visible key, also the rows past the end that
+  // re-read it (their probabilities are zero, but a value read before the
+  // store may be any bits, and 0 * NaN would reach the output).
   auto patch_new_row = [&](char* sl, int key0) __attribute__((always_inline)) {
-    const int r = slot - key0;
     const int pc = lane & 31;                            // 16-byte piece
     const bool is_v = lane >= 32;
-    const int sw = is_v ? ((2 * r) & 15) : r;
-    char* dst = sl + (is_v ? kChunkBytes : 0) + (r >> 1) * 1024 + ((r & 1) * 32 + (pc ^ sw)) * 16;
-    *(uint4*)dst = *(const uint4*)&newrow[is_v ? 1 : 0][pc * 8];
+    const uint4 val = *(const uint4*)&newrow[is_v ? 1 : 0][pc * 8];
+    const int r_end = slot == k1 - 1 ? kChunk : slot - key0 + 1;
+    for (int r = slot - key0; r < r_end; ++r) {
+      const int sw = is_v ? ((2 * r) & 15) : r;
+      *(uint4*)(sl + (is_v ? kChunkBytes : 0) + (r >> 1) * 1024 + ((r & 1) * 32 + (pc ^ sw)) * 16) = val;
+    }
   };
   auto compute = [&](char* sl, int c) __attribute__((always_inline)) {
     const int key0 = k0 + c * kChunk;

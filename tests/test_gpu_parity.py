@@ -371,6 +371,57 @@ def test_decode_wide_grid_partial_rings_and_invalid_positions():
         check_bf16_values(f"decode key b={b}", cache.k[b, :, int(slots[i])].cpu(), k_hat[i])
 
 
+def _poisoned(c, valid):
+    """A copy of cache tensor c whose slots outside `valid` ([B, cap] bool)
+    hold NaN in K-like and +Inf in V-like tensors: memory a caller never
+    wrote may hold any bits, and no such slot may reach the output."""
+    g = c.clone()
+    bits = g.view(torch.int16)
+    bad = torch.as_tensor(~valid)[:, None, :, None].expand_as(bits)
+    bits[bad] = 0x7FC0
+    bits[1::2][bad[1::2]] = 0x7F80   # odd sequences get +Inf instead
+    return g
+
+
+def test_unwritten_cache_slots_holding_nan_or_inf_are_never_read():
+    # decode over partial rings and over a linear cache, slot p itself
+    # poisoned too (the kernel writes the new token there before use)
+    for layer, kind, cap, pos in [("sliding", "ring", 512, [0, 5, 300, 510]),
+                                  ("full", "linear", 1000, [0, 63, 64, 700])]:
+        B = len(pos)
+        desc = hb.layer_desc(layer)
+        inp = synth.decode_inputs(B, 16, 4, seed=31)
+        ck = synth.cache_tensor(B, 4, cap, seed=900)
+        cv = synth.cache_tensor(B, 4, cap, seed=901)
+        valid = np.arange(cap)[None, :] < np.asarray(pos)[:, None]
+        cache = hb.KVCache(_poisoned(ck, valid).to(DEV), _poisoned(cv, valid).to(DEV), kind)
+        d = to_dev(inp)
+        out = hb.hattn_decode(desc, d["q"], d["k"], d["v"], d["gate"], torch.as_tensor(pos, dtype=torch.int32).to(DEV),
+                              max(pos), cache)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out.float()).all(), f"decode {kind}: non-finite output"
+        ref, slots, k_hat = oracle_decode(desc, inp, ck, cv, np.asarray(pos), kind)
+        check(f"decode {kind} over poisoned unwritten slots", out.cpu(), ref)
+        check_decode_cache(cache, inp, slots, k_hat)
+    # prefill: a linear cache and a ring whose slots past the history are poisoned
+    for layer, kind, cap, start, S in [("full", "linear", 200, [0, 100], 50), ("sliding", "ring", 512, [0, 300], 40)]:
+        B = len(start)
+        desc = hb.layer_desc(layer)
+        inp = synth.prefill_inputs(B, S, 16, 4, seed=32)
+        ck = synth.cache_tensor(B, 4, cap, seed=902)
+        cv = synth.cache_tensor(B, 4, cap, seed=903)
+        valid = np.arange(cap)[None, :] < np.asarray(start)[:, None]
+        clean_k = torch.where(torch.as_tensor(valid)[:, None, :, None], ck, torch.zeros_like(ck))
+        clean_v = torch.where(torch.as_tensor(valid)[:, None, :, None], cv, torch.zeros_like(cv))
+        cache = hb.KVCache(_poisoned(ck, valid).to(DEV), _poisoned(cv, valid).to(DEV), kind)
+        d = to_dev(inp)
+        out = hb.hattn_prefill(desc, d["q"], d["k"], d["v"], d["gate"], start, cache)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out.float()).all(), f"prefill {kind}: non-finite output"
+        ref, _ = oracle_prefill(desc, inp, clean_k, clean_v, start, kind, cap)
+        check(f"prefill {kind} over poisoned unwritten slots", out.cpu(), ref)
+
+
 # ------------------------------------------------------------------ chunked prefill, 1.7B shape
 @pytest.mark.parametrize("layer", ["full", "sliding"])
 def test_chunked_prefill_1p7b_shape_sampled(layer):
