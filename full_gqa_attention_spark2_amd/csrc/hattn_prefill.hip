@@ -74,6 +74,13 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Two floats to packed bf16 (low half first), rounded to nearest even by
+// the hardware conversion (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)lo, (__bf16)hi});
+}
+
 __device__ __forceinline__ void unpack8(uint4 u, float* x) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -191,10 +198,13 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   auto load_k = [&](int t, char* slot) __attribute__((always_inline)) { load_tile(krs, k_chunk0, k_chunk1, t, slot); };
   auto load_v = [&](int t, char* slot) __attribute__((always_inline)) { load_tile(vrs, v_chunk, v_chunk, t, slot); };
 
-  // Start the first tiles moving before the query prologue.
-  load_k(t_lo, k_lds0);
-  if (nt > 1) load_k(t_lo + 1, k_lds1);
-  load_v(t_lo, v_lds0);
+  // The first tiles: requested right after the query loads below, so they
+  // are in flight during the query RoPE.
+  auto load_first_tiles = [&]() __attribute__((always_inline)) {
+    load_k(t_lo, k_lds0);
+    if (nt > 1) load_k(t_lo + 1, k_lds1);
+    load_v(t_lo, v_lds0);
+  };
 
   // ---- queries: RoPE in fp32 from the cos/sin table, then bf16 fragments
   // (B operand of S^T): lane holds query lane % 32, channels
@@ -210,27 +220,74 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
     const uint16_t* qp = a.q + (((size_t)b * a.S + qr) * a.Hq + h) * kHeadDim;
     const int half = a.r >> 1;
     const float2* tp = a.table + ((size_t)b * a.S + qr) * half;
+    // With r a multiple of 32 (the pages' 64 and 256), the partner of
+    // fragment ks (channels 16ks + 8(lane/32) ..) is fragment ks +- r/32 of
+    // the same lane: every load is issued up front, in one round trip, and
+    // the rotation runs on registers.
+    auto rope_fast = [&](auto np) __attribute__((always_inline)) {
+      constexpr int NP = decltype(np)::value;  // rotated fragment pairs (ks, ks + NP)
+      uint4 raw[16];
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      const int d0 = ks * 16 + (lane >> 5) * 8;
-      float x[8];
-      unpack8(*(const uint4*)(qp + d0), x);
-      if (d0 < a.r) {
-        const bool first = d0 < half;
-        float xp[8];
-        unpack8(*(const uint4*)(qp + (first ? d0 + half : d0 - half)), xp);
-        const float2* cs = tp + (first ? d0 : d0 - half);
+      for (int ks = 0; ks < 16; ++ks) raw[ks] = *(const uint4*)(qp + ks * 16 + (lane >> 5) * 8);
+      uint4 cs[NP > 0 ? NP : 1][4];  // (cos, sin) of table entries 16p + 8(lane/32) + 0..7
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float2 t = cs[j];
-          x[j] = first ? x[j] * t.x - xp[j] * t.y : x[j] * t.x + xp[j] * t.y;
+      for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) cs[pp][u] = *(const uint4*)(tp + pp * 16 + (lane >> 5) * 8 + 2 * u);
+      load_first_tiles();
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        float x[8];
+        unpack8(raw[ks], x);
+        if (ks < 2 * NP) {
+          const bool first = ks < NP;
+          const int pp = first ? ks : ks - NP;
+          float xp[8];
+          unpack8(raw[first ? ks + NP : ks - NP], xp);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint4 w = cs[pp][j >> 1];
+            const float2 t = (j & 1) ? make_float2(__uint_as_float(w.z), __uint_as_float(w.w))
+                                     : make_float2(__uint_as_float(w.x), __uint_as_float(w.y));
+            x[j] = first ? x[j] * t.x - xp[j] * t.y : x[j] * t.x + xp[j] * t.y;
+          }
         }
-      }
-      bf16x8 v;
+        bf16x8 v;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = (__bf16)(qvalid ? x[j] : 0.f);
-      qf[ks] = v;
-    }
+        for (int j = 0; j < 8; ++j) v[j] = (__bf16)(qvalid ? x[j] : 0.f);
+        qf[ks] = v;
+      }
+    };
+    // Any other r (a multiple of 16): fragment by fragment, partners and
+    // table entries loaded per fragment.
+    auto rope_generic = [&]() __attribute__((always_inline)) {
+      load_first_tiles();
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        const int d0 = ks * 16 + (lane >> 5) * 8;
+        float x[8];
+        unpack8(*(const uint4*)(qp + d0), x);
+        if (d0 < a.r) {
+          const bool first = d0 < half;
+          float xp[8];
+          unpack8(*(const uint4*)(qp + (first ? d0 + half : d0 - half)), xp);
+          const float2* cs = tp + (first ? d0 : d0 - half);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float2 t = cs[j];
+            x[j] = first ? x[j] * t.x - xp[j] * t.y : x[j] * t.x + xp[j] * t.y;
+          }
+        }
+        bf16x8 v;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = (__bf16)(qvalid ? x[j] : 0.f);
+        qf[ks] = v;
+      }
+    };
+    if (a.r == 64) rope_fast(std::integral_constant<int, 2>{});
+    else if (a.r == 256) rope_fast(std::integral_constant<int, 8>{});
+    else if (a.r == 0) rope_fast(std::integral_constant<int, 0>{});
+    else rope_generic();
     // The fragments are only ever MFMA operands: keep them in the
     // accumulation registers, which leaves the VGPRs to the softmax.
 #pragma unroll
@@ -450,21 +507,33 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   l_i = pair_sum(l_i);
 
   // ---- epilogue: divide by the softmax sum, gate in fp32, one bf16 store.
-  // acc[db] register i holds channel db*32 + 8*(i/4) + 4*(lane/32) + i%4.
-  if (qvalid) {
+  // acc[db] register i holds channel db*32 + 8*(i/4) + 4*(lane/32) + i%4 of
+  // query lane % 32. The rows go through LDS so that each store instruction
+  // writes two whole 512-byte rows: wave w stages its 32 rows in 16 KiB of
+  // the K slots, which no wave reads any more (the barrier before the last
+  // P.V lies behind every S stream; the last P.V reads V slots only). Row r
+  // keeps its 16-byte chunk c at position c ^ r, so neither the 8-byte
+  // writes nor the 16-byte reads collide on banks.
+  {
     const float g = bf16_bits_to_float(gate_bits);
     const float f = (1.0f / l_i) * (1.0f / (1.0f + expf(-g)));
-    uint16_t* op = a.out + orow * kHeadDim + 4 * (lane >> 5);
+    char* stage = (wave < 2 ? k_lds0 : k_lds1) + (wave & 1) * 16384;
+    const int row = lane & 31;
 #pragma unroll
     for (int db = 0; db < 8; ++db)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint32_t w0 = (uint32_t)float_to_bf16_bits(acc[db][4 * c + 0] * f) |
-                            ((uint32_t)float_to_bf16_bits(acc[db][4 * c + 1] * f) << 16);
-        const uint32_t w1 = (uint32_t)float_to_bf16_bits(acc[db][4 * c + 2] * f) |
-                            ((uint32_t)float_to_bf16_bits(acc[db][4 * c + 3] * f) << 16);
-        *(uint2*)(op + db * 32 + 8 * c) = make_uint2(w0, w1);
+        const uint32_t w0 = pack_bf16x2(acc[db][4 * c + 0] * f, acc[db][4 * c + 1] * f);
+        const uint32_t w1 = pack_bf16x2(acc[db][4 * c + 2] * f, acc[db][4 * c + 3] * f);
+        *(uint2*)(stage + row * 512 + (((db * 4 + c) ^ row) << 4) + (lane >> 5) * 8) = make_uint2(w0, w1);
       }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int r = 2 * k + (lane >> 5);
+      const uint4 v = *(const uint4*)(stage + r * 512 + (((lane & 31) ^ r) << 4));
+      if (q0 + r < a.S)
+        *(uint4*)(a.out + (((size_t)b * a.S + q0 + r) * a.Hq + h) * kHeadDim + (lane & 31) * 8) = v;
+    }
   }
 }
 
