@@ -229,7 +229,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
       uint4 raw[16];
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) raw[ks] = *(const uint4*)(qp + ks * 16 + (lane >> 5) * 8);
-      uint4 cs[NP > 0 ? NP : 1][4];  // (cos, sin) of table entries 16p + 8(lane/32) + 0..7
+      uint4 cs[NP][4];  // (cos, sin) of table entries 16p + 8(lane/32) + 0..7
 #pragma unroll
       for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
@@ -286,7 +286,6 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
     };
     if (a.r == 64) rope_fast(std::integral_constant<int, 2>{});
     else if (a.r == 256) rope_fast(std::integral_constant<int, 8>{});
-    else if (a.r == 0) rope_fast(std::integral_constant<int, 0>{});
     else rope_generic();
     // The fragments are only ever MFMA operands: keep them in the
     // accumulation registers, which leaves the VGPRs to the softmax.

@@ -189,6 +189,34 @@ def test_prefill_small_shapes(layer, B, S, start, cap, kind):
                           k_hat[b, pos - start[b]])
 
 
+@pytest.mark.parametrize("fraction", [0.0625, 0.5])
+def test_prefill_and_decode_other_rotary_widths(fraction):
+    # r = 16 (RoPE partners in the other half of the wave) and 128 (same
+    # lane, no specialised prologue): the general query path
+    desc = hb.layer_desc("full", rotary_fraction=fraction)
+    B, S = 2, 90
+    inp = synth.prefill_inputs(B, S, 16, 4, seed=41)
+    ck = torch.zeros((B, 4, 128, 256), dtype=torch.bfloat16)
+    cv = torch.zeros_like(ck)
+    cache = hb.KVCache(ck.to(DEV), cv.to(DEV), "linear")
+    d = to_dev(inp)
+    out = hb.hattn_prefill(desc, d["q"], d["k"], d["v"], d["gate"], [0, 5], cache)
+    torch.cuda.synchronize()
+    ref, k_hat = oracle_prefill(desc, inp, ck, cv, [0, 5], "linear", 128)
+    check(f"prefill rotary fraction {fraction}", out.cpu(), ref)
+    # decode of the next token on the same cache
+    dinp = synth.decode_inputs(B, 16, 4, seed=42)
+    pos = np.array([S, S + 5])
+    hk, hv = cache.k.cpu(), cache.v.cpu()
+    dd = to_dev(dinp)
+    o = hb.hattn_decode(desc, dd["q"], dd["k"], dd["v"], dd["gate"], torch.as_tensor(pos, dtype=torch.int32).to(DEV),
+                        int(pos.max()), cache)
+    torch.cuda.synchronize()
+    ref_d, slots, k_hat_d = oracle_decode(desc, dinp, hk, hv, pos, "linear")
+    check(f"decode rotary fraction {fraction}", o.cpu(), ref_d)
+    check_decode_cache(cache, dinp, slots, k_hat_d)
+
+
 def test_prefill_window_one_and_peaky():
     desc, inp, ck, cv, cache, out = run_prefill("sliding", 1, 300, 16, 4, [0], 4, "linear", 300, window=1)
     ref, _ = oracle_prefill(desc, inp, ck, cv, [0], "linear", 300)
