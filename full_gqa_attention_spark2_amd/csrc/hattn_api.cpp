@@ -289,7 +289,7 @@ int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k, co
   }
 
   // 2. cos/sin table of the new positions; rotated K and V -> cache slots
-  //    (linear) or staging rows (ring)
+  //    (linear) or staging rows and the ring's slots (ring)
   PrefillPrepArgs ra{};
   ra.k = (const uint16_t*)k;
   ra.v = (const uint16_t*)v;
@@ -301,6 +301,12 @@ int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k, co
   ra.Hkv = Hkv;
   ra.dst_rows = ring ? L.stage_rows : cache->capacity;
   ra.r = r;
+  // a ring keeps the last min(S, capacity) new tokens; the prep kernel
+  // writes them to their slots (the history it replaces is already staged)
+  ra.ring_k = ring ? (uint16_t*)cache->k : nullptr;
+  ra.ring_v = ring ? (uint16_t*)cache->v : nullptr;
+  ra.ring_cap = cache->capacity;
+  ra.ring_from = ring ? seq_len - std::min(seq_len, cache->capacity) : seq_len;
   fill_inv_freq(desc->rope_theta, r, ra.inv_freq);
   PrefillAttnArgs aa{};
   for (int b = 0; b < batch; ++b) {
@@ -334,18 +340,6 @@ int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k, co
   profile_end(prof, stream);
   if (e != hipSuccess) return HATTN_ERR_LAUNCH;
 
-  // 4. a ring keeps the last min(S, capacity) new tokens
-  if (ring) {
-    for (int b = 0; b < batch; ++b) {
-      const int hist = std::min(start_pos[b], w - 1);
-      const int keep = std::min(seq_len, cache->capacity);
-      rc.count[b] = keep;
-      rc.first_pos[b] = start_pos[b] + seq_len - keep;
-      rc.stage_row0[b] = hist + seq_len - keep;
-    }
-    e = launch_stage_to_ring(rc, stream);
-    if (e != hipSuccess) return HATTN_ERR_LAUNCH;
-  }
   return HATTN_OK;
 }
 

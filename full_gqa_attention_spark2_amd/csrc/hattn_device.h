@@ -27,24 +27,19 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
-// fp64 -> bf16 with a single rounding (nearest, ties to even): the value is
-// cut to 8 significant bits in fp64, which is then exact in fp32.
+// fp64 -> bf16 with a single rounding (nearest, ties to even). x is first
+// rounded to fp32 with round-to-odd (truncate, then set the last bit when
+// anything was cut), then to bf16 by the hardware's round-to-nearest-even:
+// with 24 >= 8 + 2 significant bits in between, the two roundings give the
+// correctly rounded result (the round-to-odd lemma). Branch-free; NaN stays
+// NaN, infinities and overflow go to infinity.
 __device__ __forceinline__ uint16_t double_to_bf16_bits(double x) {
-  if (!(fabs(x) <= 1.7976931348623157e308)) {  // inf or NaN
-    float f = (float)x;
-    return (uint16_t)(__float_as_uint(f) >> 16 | ((x != x) ? 0x40u : 0u));
-  }
-  if (x == 0.0) return (uint16_t)(__float_as_uint((float)x) >> 16);  // keeps sign
-  double r;
-  if (fabs(x) < 0x1p-126) {
-    r = ldexp(rint(ldexp(x, 133)), -133);  // bf16 subnormal spacing 2^-133
-  } else {
-    int e;
-    double m = frexp(x, &e);                // |m| in [0.5, 1)
-    r = ldexp(rint(ldexp(m, 8)), e - 8);
-  }
-  if (fabs(r) > 0x1.fep127) r = copysign(__builtin_inf(), r);
-  return (uint16_t)(__float_as_uint((float)r) >> 16);
+  const float f = (float)x;  // nearest even
+  const double back = (double)f;
+  uint32_t u = __float_as_uint(f);
+  u -= (fabs(back) > fabs(x)) ? 1u : 0u;  // rounded away from zero: step back
+  u |= (back != x) ? 1u : 0u;             // inexact: odd
+  return float_to_bf16_bits(__uint_as_float(u));
 }
 
 // ---------------------------------------------------------------- RoPE

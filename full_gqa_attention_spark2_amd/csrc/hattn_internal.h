@@ -24,6 +24,10 @@ struct PrefillPrepArgs {
   int B, S, Hkv;
   int dst_rows;     // rows per (b, kv head) in dst
   int r;            // rotated channels
+  uint16_t* ring_k; // ring cache that also receives tokens >= ring_from (or null)
+  uint16_t* ring_v;
+  int ring_cap;
+  int ring_from;
   double inv_freq[128];
   int start[kMaxPrefillBatch];    // position of token 0 of sequence b
   int dst_row0[kMaxPrefillBatch]; // dst row of token 0 of sequence b
@@ -92,7 +96,6 @@ struct ProbeArgs {
 
 hipError_t launch_prefill_prep(const PrefillPrepArgs& a, hipStream_t s);
 hipError_t launch_ring_to_stage(const RingCopyArgs& a, hipStream_t s);
-hipError_t launch_stage_to_ring(const RingCopyArgs& a, hipStream_t s);
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_rope_apply(const RopeApplyArgs& a, hipStream_t s);

@@ -10,57 +10,95 @@
 
 namespace hattn {
 
-// Rotated value of channel d of one head (x points at the head's 256-channel
-// row): channel i < r/2 pairs with i + r/2.
-__device__ __forceinline__ uint16_t rotate_channel(const uint16_t* x, int d, int half, int r,
-                                                   const double* cs, const double* sn) {
-  if (d >= r) return x[d];
-  double a = (double)bf16_bits_to_float(x[d]);
-  double y;
-  if (d < half) {
-    double b = (double)bf16_bits_to_float(x[d + half]);
-    y = a * cs[d] - b * sn[d];
-  } else {
-    double b = (double)bf16_bits_to_float(x[d - half]);
-    y = a * cs[d - half] + b * sn[d - half];
-  }
-  return double_to_bf16_bits(y);
-}
-
 // One block per (new token, sequence): the token's cos/sin table row, its
-// rotated keys (fp64 rotation, one bf16 rounding) and its values.
-__global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillPrepArgs a) {
-  __shared__ double cs[128];
-  __shared__ double sn[128];
-  const int i = blockIdx.x;
+// rotated keys (fp64 rotation, one bf16 rounding) and its values, written to
+// the destination rows and, for a ring, when the token is among the last
+// min(S, capacity), also to its ring slot. Each thread takes 16-byte chunks
+// (8 channels of one head); the loads go out before the angles are
+// evaluated.
+constexpr int kPrepTokens = 1;
+constexpr int kPrepThreads = 128;
+
+__global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(PrefillPrepArgs a) {
+  __shared__ double cs[kPrepTokens][128];
+  __shared__ double sn[kPrepTokens][128];
+  const int i0 = blockIdx.x * kPrepTokens;
   const int b = blockIdx.y;
   const int t = threadIdx.x;
-  const int p = a.start[b] + i;
   const int half = a.r >> 1;
-  if (t < half) {
+  const int ntok = min(kPrepTokens, a.S - i0);
+  const int nchunk = ntok * a.Hkv * 32;
+
+  // chunk c: token c / (32 Hkv), head (c / 32) % Hkv, channels 8(c % 32) .. +7
+  auto src_off = [&](int c) { return (((size_t)b * a.S + i0 + c / (a.Hkv * 32)) * a.Hkv + (c >> 5) % a.Hkv) * kHeadDim; };
+  auto partner = [&](int ch) {  // chunk holding the RoPE partners of chunk ch
+    const int d0 = ch * 8;
+    return d0 < a.r ? (d0 < half ? d0 + half : d0 - half) >> 3 : ch;
+  };
+  auto finish = [&](int c, uint4 kx, uint4 kp, uint4 vx) {
+    const int tok = c / (a.Hkv * 32), h = (c >> 5) % a.Hkv, ch = c & 31;
+    const int d0 = ch * 8;
+    uint4 ko = kx;
+    if (d0 < a.r) {
+      const uint16_t* x = (const uint16_t*)&kx;
+      const uint16_t* xp = (const uint16_t*)&kp;
+      uint16_t* y = (uint16_t*)&ko;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int d = d0 + j;
+        const double u = (double)bf16_bits_to_float(x[j]);
+        const double w = (double)bf16_bits_to_float(xp[j]);
+        y[j] = d < half ? double_to_bf16_bits(u * cs[tok][d] - w * sn[tok][d])
+                        : double_to_bf16_bits(u * cs[tok][d - half] + w * sn[tok][d - half]);
+      }
+    }
+    const int i = i0 + tok;
+    const size_t o = (((size_t)b * a.Hkv + h) * a.dst_rows + a.dst_row0[b] + i) * kHeadDim;
+    ((uint4*)(a.dst_k + o))[ch] = ko;
+    ((uint4*)(a.dst_v + o))[ch] = vx;
+    if (a.ring_k && i >= a.ring_from) {
+      const int slot = (a.start[b] + i) % a.ring_cap;
+      const size_t ro = (((size_t)b * a.Hkv + h) * a.ring_cap + slot) * kHeadDim;
+      ((uint4*)(a.ring_k + ro))[ch] = ko;
+      ((uint4*)(a.ring_v + ro))[ch] = vx;
+    }
+  };
+
+  // first round of chunks: loads first
+  uint4 kx[2], kp[2], vx[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int c = t + kPrepThreads * u;
+    if (c < nchunk) {
+      const size_t off = src_off(c);
+      kx[u] = ((const uint4*)(a.k + off))[c & 31];
+      kp[u] = ((const uint4*)(a.k + off))[partner(c & 31)];
+      vx[u] = ((const uint4*)(a.v + off))[c & 31];
+    }
+  }
+  for (int e = t; e < ntok * half; e += kPrepThreads) {
+    const int tok = e / half, j = e % half;
     double s, c;
-    rope_sincos(p, a.inv_freq[t], &s, &c);
-    cs[t] = c;
-    sn[t] = s;
-    a.table[((size_t)b * a.S + i) * half + t] = make_float2((float)c, (float)s);
+    rope_sincos(a.start[b] + i0 + tok, a.inv_freq[j], &s, &c);
+    cs[tok][j] = c;
+    sn[tok][j] = s;
+    a.table[((size_t)b * a.S + i0 + tok) * half + j] = make_float2((float)c, (float)s);
   }
   __syncthreads();
-  const size_t kbase = ((size_t)b * a.S + i) * a.Hkv * kHeadDim;
-  const int row = a.dst_row0[b] + i;
-  for (int e = t; e < a.Hkv * kHeadDim; e += 256) {
-    const int h = e >> 8, d = e & 255;
-    const size_t o = (((size_t)b * a.Hkv + h) * a.dst_rows + row) * kHeadDim + d;
-    a.dst_k[o] = rotate_channel(a.k + kbase + (size_t)h * kHeadDim, d, half, a.r, cs, sn);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int c = t + kPrepThreads * u;
+    if (c < nchunk) finish(c, kx[u], kp[u], vx[u]);
   }
-  for (int c = t; c < a.Hkv * 32; c += 256) {  // values: 16-byte chunks
-    const int h = c >> 5, ch = c & 31;
-    const size_t o = (((size_t)b * a.Hkv + h) * a.dst_rows + row) * kHeadDim;
-    ((uint4*)(a.dst_v + o))[ch] = ((const uint4*)(a.v + kbase + (size_t)h * kHeadDim))[ch];
+  for (int c = t + 2 * kPrepThreads; c < nchunk; c += kPrepThreads) {  // more than 8 KV heads
+    const size_t off = src_off(c);
+    finish(c, ((const uint4*)(a.k + off))[c & 31], ((const uint4*)(a.k + off))[partner(c & 31)],
+           ((const uint4*)(a.v + off))[c & 31]);
   }
 }
 
-// One block per (copied row, sequence): all KV heads, K and V, 16 B per lane.
-template <bool kToStage>
+// A ring's visible history into the staging rows: one block per (copied
+// row, sequence), all KV heads, K and V, 16 B per lane.
 __global__ __launch_bounds__(256) void ring_copy_kernel(RingCopyArgs a) {
   const int j = blockIdx.x;
   const int b = blockIdx.y;
@@ -77,7 +115,7 @@ __global__ __launch_bounds__(256) void ring_copy_kernel(RingCopyArgs a) {
     uint16_t* stage = kv ? a.stage_v : a.stage_k;
     uint4* rp = (uint4*)(ring + (((size_t)b * a.Hkv + h) * a.cap + slot) * kHeadDim) + ch;
     uint4* sp = (uint4*)(stage + (((size_t)b * a.Hkv + h) * a.stage_rows + srow) * kHeadDim) + ch;
-    if (kToStage) *sp = *rp; else *rp = *sp;
+    *sp = *rp;
   }
 }
 
@@ -117,7 +155,8 @@ __global__ __launch_bounds__(256) void index_probe_kernel(ProbeArgs a) {
 }
 
 hipError_t launch_prefill_prep(const PrefillPrepArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(prefill_prep_kernel, dim3(a.S, a.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(prefill_prep_kernel, dim3((a.S + kPrepTokens - 1) / kPrepTokens, a.B), dim3(kPrepThreads), 0, s,
+                     a);
   return hipGetLastError();
 }
 
@@ -130,14 +169,7 @@ static int max_count(const RingCopyArgs& a) {
 hipError_t launch_ring_to_stage(const RingCopyArgs& a, hipStream_t s) {
   const int m = max_count(a);
   if (m == 0) return hipSuccess;
-  hipLaunchKernelGGL(ring_copy_kernel<true>, dim3(m, a.B), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_stage_to_ring(const RingCopyArgs& a, hipStream_t s) {
-  const int m = max_count(a);
-  if (m == 0) return hipSuccess;
-  hipLaunchKernelGGL(ring_copy_kernel<false>, dim3(m, a.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(ring_copy_kernel, dim3(m, a.B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
