@@ -120,8 +120,9 @@ size_t hattn_prefill_workspace_size(const hattn_layer_desc* desc,
  *     0 .. start_pos[b]-1 and have capacity >= start_pos[b] + S. A ring
  *     cache must hold positions up to start_pos[b]-1 as ring slots.
  *   out:  bf16 [B][S][num_q_heads][256]; must not alias any input.
- * The rotated keys and the values of the new tokens are written to the cache
- * (a ring keeps the last min(S, capacity) of them). B <= 128, and the key
+ * Cache slots outside the history may hold any bits, NaN included; they
+ * never reach the result. The rotated keys and the values of the new tokens
+ * are written to the cache (a ring keeps the last min(S, capacity) of them). B <= 128, and the key
  * rows of one (sequence, KV head) -- a linear cache's capacity, or
  * window - 1 + S for a ring -- must not exceed 2^23; larger calls return
  * HATTN_ERR_UNSUPPORTED. */
@@ -142,9 +143,11 @@ size_t hattn_decode_workspace_size(const hattn_layer_desc* desc,
  *   pos:  int32 [B], DEVICE memory; max_pos: a host upper bound of pos[]
  *     (checked against a linear cache's capacity).
  *   out:  bf16 [B][num_q_heads][256]
- * The cache must hold positions 0 .. pos[b]-1. The new rotated key and value
- * are written to their slot before attention reads the cache. A pos[b]
- * outside [0, max_pos] yields a NaN output row and no cache write. */
+ * The cache must hold positions 0 .. pos[b]-1 (slots outside the visible
+ * range may hold any bits, NaN included; they never reach the result). The
+ * new rotated key and value are written to their slot, and the attention
+ * includes them. A pos[b] outside [0, max_pos] yields a NaN output row and
+ * no cache write. */
 int hattn_decode(const hattn_layer_desc* desc, const void* q, const void* k,
                  const void* v, const void* gate, int32_t batch,
                  const int32_t* pos, int32_t max_pos,
