@@ -14,15 +14,15 @@
 // The transposed orientation keeps a query's running max, sum and rescale
 // factor in one lane.
 //
-// K and V tiles go from global memory straight into LDS (global_load_lds,
-// 16 B per lane) in the order the MFMA reads them, so every LDS read is a
-// contiguous, conflict-free 512 B per half-wave at "lane base + constant".
-// Two K slots and two V slots form a pipeline: step t computes S(t) and
-// issues P(t-1).V(t-1), so the softmax of tile t (VALU) runs while the
-// matrix cores work on P.V of tile t-1, and tiles t+1 (K) and t (V) load
-// meanwhile. The running max is only moved (and O rescaled) when a tile's max
-// exceeds it by more than 2^8, so most tiles skip the rescale; the step body
-// has no branch between its MFMAs and its softmax.
+// K and V tiles go from global memory straight into LDS by LDS DMA (buffer
+// loads, 16 B per lane; each instruction fills one 1 KiB block from eight
+// whole 128-byte lines) in a swizzled layout that keeps the MFMA fragment
+// reads free of bank conflicts. Two K slots and two V slots form a pipeline:
+// step t runs S(t+1) and P(t-1).V(t-1) on the matrix cores while the VALU
+// computes the softmax of tile t, and K(t+2) and V(t) load meanwhile. The
+// running max is only moved (and O rescaled) when a tile's max exceeds it by
+// more than 2^8, so most tiles skip the rescale; the step body has no branch
+// between its MFMAs and its softmax.
 #include <type_traits>
 
 #include "hattn_device.h"
