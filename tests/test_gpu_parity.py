@@ -450,6 +450,32 @@ def test_unwritten_cache_slots_holding_nan_or_inf_are_never_read():
         check(f"prefill {kind} over poisoned unwritten slots", out.cpu(), ref)
 
 
+def test_profiling_hook_counts_and_times_kernel_sections():
+    # the event pairs the bench reads: one per call while enabled, none after
+    desc = hb.layer_desc("full")
+    inp = to_dev(synth.prefill_inputs(1, 64, 16, 4, seed=51))
+    cache = hb.KVCache.empty(1, 4, 64, "linear")
+    hb.hattn_profile_read(hb.PROFILE_PREFILL)
+    hb.hattn_profile_read(hb.PROFILE_DECODE)
+    hb.hattn_profile_enable(True)
+    try:
+        for _ in range(3):
+            hb.hattn_prefill(desc, inp["q"], inp["k"], inp["v"], inp["gate"], [0], cache)
+        dinp = to_dev(synth.decode_inputs(1, 16, 4, seed=52))
+        big = hb.KVCache.empty(1, 4, 128, "linear")
+        hb.hattn_decode(desc, dinp["q"], dinp["k"], dinp["v"], dinp["gate"],
+                        torch.tensor([100], dtype=torch.int32, device=DEV), 100, big)
+    finally:
+        hb.hattn_profile_enable(False)
+    n, ms = hb.hattn_profile_read(hb.PROFILE_PREFILL)
+    assert n == 3 and ms > 0.0
+    n, ms = hb.hattn_profile_read(hb.PROFILE_DECODE)
+    assert n == 1 and ms > 0.0
+    hb.hattn_prefill(desc, inp["q"], inp["k"], inp["v"], inp["gate"], [0], cache)
+    torch.cuda.synchronize()
+    assert hb.hattn_profile_read(hb.PROFILE_PREFILL) == (0, 0.0)
+
+
 # ------------------------------------------------------------------ chunked prefill, 1.7B shape
 @pytest.mark.parametrize("layer", ["full", "sliding"])
 def test_chunked_prefill_1p7b_shape_sampled(layer):
