@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(HERE, "libhattn.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "hattn.h")
 
 LAYER_SLIDING, LAYER_FULL = 0, 1
+GATE_SIGMOID, GATE_SILU = 0, 1
 KV_RING, KV_LINEAR = 0, 1
 HEAD_DIM = 256
 
@@ -36,6 +37,7 @@ class LayerDesc(ctypes.Structure):
         ("num_q_heads", ctypes.c_int32),
         ("num_kv_heads", ctypes.c_int32),
         ("head_dim", ctypes.c_int32),
+        ("gate_act", ctypes.c_int32),
     ]
 
 
@@ -125,11 +127,14 @@ def _need(t, name, dtype=torch.bfloat16, shape=None):
 
 def layer_desc(layer_type, num_q_heads=16, num_kv_heads=4, **overrides) -> LayerDesc:
     """The page's parameters for a layer type ("sliding"/"full" or 0/1),
-    with optional overrides of window / rope_theta / rotary_fraction."""
+    with optional overrides of window / rope_theta / rotary_fraction /
+    gate_act ("sigmoid"/"silu" or 0/1)."""
     lt = {"sliding": LAYER_SLIDING, "full": LAYER_FULL}.get(layer_type, layer_type)
     d = LayerDesc()
     _check("hattn_layer_defaults", lib().hattn_layer_defaults(lt, num_q_heads, num_kv_heads, ctypes.byref(d)))
     for k, v in overrides.items():
+        if k == "gate_act":
+            v = {"sigmoid": GATE_SIGMOID, "silu": GATE_SILU}.get(v, v)
         setattr(d, k, v)
     return d
 

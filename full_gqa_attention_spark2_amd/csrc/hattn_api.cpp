@@ -12,6 +12,8 @@
 
 using namespace hattn;
 
+static_assert(sizeof(hattn_layer_desc) == 40, "hattn_layer_desc layout is part of the ABI");
+
 namespace {
 
 constexpr int kHeadDimSupported = 256;
@@ -41,6 +43,7 @@ int check_desc(const hattn_layer_desc* d) {
   if (d->num_q_heads % d->num_kv_heads) return HATTN_ERR_SHAPE;
   if (d->head_dim != kHeadDimSupported) return HATTN_ERR_UNSUPPORTED;
   if (d->num_q_heads / d->num_kv_heads != kGroupSupported) return HATTN_ERR_UNSUPPORTED;
+  if (d->gate_act != HATTN_GATE_SIGMOID && d->gate_act != HATTN_GATE_SILU) return HATTN_ERR_UNSUPPORTED;
   if (!(d->rope_theta > 0.0) || !isfinite(d->rope_theta)) return HATTN_ERR_ROPE;
   const int r = rotary_channels(d->rotary_fraction, d->head_dim);
   if (r < 0) return HATTN_ERR_ROPE;
@@ -334,6 +337,7 @@ int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k, co
   aa.rows = ring ? L.stage_rows : cache->capacity;
   aa.window = desc->layer_type == HATTN_LAYER_SLIDING ? w : 0;
   aa.r = r;
+  aa.gate_act = desc->gate_act;
   aa.q_tiles = (seq_len + kPrefillBlockQ - 1) / kPrefillBlockQ;
   hipEvent_t prof = profile_begin(HATTN_PROFILE_PREFILL, stream);
   e = launch_prefill_attn(aa, stream);
@@ -397,6 +401,7 @@ int hattn_decode(const hattn_layer_desc* desc, const void* q, const void* k, con
   a.window = desc->layer_type == HATTN_LAYER_SLIDING ? desc->window : 0;
   a.max_pos = max_pos;
   a.r = rotary_channels(desc->rotary_fraction, desc->head_dim);
+  a.gate_act = desc->gate_act;
   fill_inv_freq(desc->rope_theta, a.r, a.inv_freq);
   a.nsplit = p.nsplit;
   a.split_keys = p.split_keys;

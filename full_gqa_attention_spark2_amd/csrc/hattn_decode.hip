@@ -59,7 +59,6 @@ __device__ __forceinline__ void dma16(i32x4 rs, uint32_t voff, uint32_t lds) {
 __device__ __forceinline__ uint32_t lds_off(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
-__device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + expf(-g)); }
 
 // Sum / max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane groups),
 // by VALU lane swaps.
@@ -408,7 +407,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     const int h = kvh * kGroup + hh;
     if (a.nsplit == 1) {
       const float g = bf16_bits_to_float(gate_bits[hh]);
-      a.out[((size_t)b * a.Hq + h) * kHeadDim + d] = float_to_bf16_bits(O[hh] / L[hh] * sigmoidf_(g));
+      a.out[((size_t)b * a.Hq + h) * kHeadDim + d] = float_to_bf16_bits(O[hh] / L[hh] * gate_factor(g, a.gate_act));
     } else {
       const size_t pi = ((size_t)b * a.Hq + h) * a.nsplit + sp;
       a.part_o[pi * kHeadDim + d] = O[hh];
@@ -480,7 +479,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   if (g == 0) {
     const float O = ((acc + part[0][d]) + part[1][d]) + part[2][d];
     const float gl = bf16_bits_to_float(a.gate[(size_t)b * a.Hq + h]);
-    o[d] = float_to_bf16_bits(O / L * sigmoidf_(gl));
+    o[d] = float_to_bf16_bits(O / L * gate_factor(gl, a.gate_act));
   }
 }
 

@@ -98,6 +98,14 @@ __device__ __forceinline__ void decode_key_range(int p, int ring, int cap, int w
   }
 }
 
+// ---------------------------------------------------------------- gate
+// The per-head output gate factor in fp32: sigmoid(g) (act 0), or
+// silu(g) = g * sigmoid(g) (act 1).
+__device__ __forceinline__ float gate_factor(float g, int act) {
+  const float s = 1.0f / (1.0f + expf(-g));
+  return act ? g * s : s;
+}
+
 // ---------------------------------------------------------------- misc
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

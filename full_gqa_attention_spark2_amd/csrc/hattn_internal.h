@@ -57,6 +57,7 @@ struct PrefillAttnArgs {
   int window;             // <= 0: unbounded
   int r;                  // rotated channels (multiple of 16)
   int q_tiles;            // ceil(S / kPrefillBlockQ)
+  int gate_act;           // 0 sigmoid, 1 silu
   int start[kMaxPrefillBatch];     // position of query 0
   int key_pos0[kMaxPrefillBatch];  // position held by key row 0
   int n_keys[kMaxPrefillBatch];    // valid key rows
@@ -77,6 +78,7 @@ struct DecodeArgs {
   int r;
   int nsplit;
   int split_keys;         // keys per split, multiple of 128
+  int gate_act;           // 0 sigmoid, 1 silu
   double inv_freq[128];
 };
 

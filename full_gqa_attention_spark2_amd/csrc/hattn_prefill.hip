@@ -1,5 +1,6 @@
 // Flash-style prefill attention for gfx950 (page "Spark-X2.5 架构（4B / 1.7B）",
-// §3 Eq. 1: softmax(Q K^T / sqrt(256)) V times a per-head sigmoid gate; §2:
+// §3 Eq. 1: softmax(Q K^T / sqrt(256)) V times a per-head gate (sigmoid, or silu,
+// the alternative the section mentions); §2:
 // causal mask, plus the 512-token window on sliding layers; §4: the queries'
 // partial RoPE).
 //
@@ -515,7 +516,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   // writes nor the 16-byte reads collide on banks.
   {
     const float g = bf16_bits_to_float(gate_bits);
-    const float f = (1.0f / l_i) * (1.0f / (1.0f + expf(-g)));
+    const float f = (1.0f / l_i) * gate_factor(g, a.gate_act);
     char* stage = (wave < 2 ? k_lds0 : k_lds1) + (wave & 1) * 16384;
     const int row = lane & 31;
 #pragma unroll

@@ -10,6 +10,8 @@
  *     (partial_rotary_factor 0.25) with theta = 5e6.
  *   - §3 逐头输出门控, Eq. 1: out = softmax(Q K^T / sqrt(d_head)) V, multiplied
  *     by sigmoid of one gate logit per (token, head) in fp32, stored as bf16.
+ *     The same section notes that the model code also offers a silu gate
+ *     activation (g * sigmoid(g)); the released checkpoints use sigmoid.
  *   - §1 config table: 16 query heads share 4 KV heads (8 / 2 for the 1.7B
  *     shape), head_dim 256, bf16.
  *   - §6 KV table: full layers keep every token, sliding layers only the last
@@ -59,7 +61,7 @@ typedef enum {
   HATTN_OK = 0,
   HATTN_ERR_NULL = -1,        /* a required pointer is NULL                     */
   HATTN_ERR_SHAPE = -2,       /* a size is <= 0 or inconsistent                 */
-  HATTN_ERR_UNSUPPORTED = -3, /* head_dim != 256 or group size != 4             */
+  HATTN_ERR_UNSUPPORTED = -3, /* head_dim != 256, group != 4, unknown gate_act  */
   HATTN_ERR_ROPE = -4,        /* theta <= 0 or head_dim*fraction not even int   */
   HATTN_ERR_WINDOW = -5,      /* sliding layer with window < 1, full with > 0   */
   HATTN_ERR_CACHE = -6,       /* cache kind/capacity/batch does not fit layer   */
@@ -71,6 +73,10 @@ typedef enum {
 } hattn_status;
 
 typedef enum { HATTN_LAYER_SLIDING = 0, HATTN_LAYER_FULL = 1 } hattn_layer_type;
+/* Activation of the per-head output gate (page §3 逐头输出门控): sigmoid(g),
+ * as in Eq. 1 and both released checkpoints, or silu(g) = g * sigmoid(g),
+ * the alternative gate mode the model code supports. Evaluated in fp32. */
+typedef enum { HATTN_GATE_SIGMOID = 0, HATTN_GATE_SILU = 1 } hattn_gate_act;
 typedef enum { HATTN_KV_RING = 0, HATTN_KV_LINEAR = 1 } hattn_kv_kind;
 
 /* Parameters of one attention layer (page §1 config table, §2, §4 table). */
@@ -82,6 +88,7 @@ typedef struct {
   int32_t num_q_heads;     /* 16 (4B) or 8 (1.7B)                               */
   int32_t num_kv_heads;    /* 4 (4B) or 2 (1.7B)                                */
   int32_t head_dim;        /* 256                                               */
+  int32_t gate_act;        /* hattn_gate_act; 0 (sigmoid) unless set            */
 } hattn_layer_desc;
 
 /* A caller-owned KV cache of one layer. */

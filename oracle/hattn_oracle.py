@@ -39,7 +39,10 @@ Readings taken where the pages are silent (each is repeated where it is used):
 * GQA: q-head h reads kv-head h // (Hq / Hkv).
 * Scale 1/sqrt(256) = 1/16, no softcap, no q/k norm.
 * The gate is sigmoid of one logit per (token, head), broadcast over the
-  head's channels; the oracle's output is the unrounded fp64 product.
+  head's channels; the oracle's output is the unrounded fp64 product. [SPARK
+  §3] also notes that the model code accepts a silu gate activation; it is
+  read as silu(g) = g * sigmoid(g) in place of sigmoid(g), nothing else
+  changed.
 * Ring slot of position p is p mod capacity; a ring requires capacity == w.
 """
 from __future__ import annotations
@@ -127,6 +130,20 @@ def sigmoid(g) -> np.ndarray:
     return 1.0 / (1.0 + np.exp(-g))
 
 
+GATE_ACTS = ("sigmoid", "silu")
+
+
+def gate_factor(g, gate_act: str = "sigmoid") -> np.ndarray:
+    """The per-head output gate [SPARK §3 Eq. 1]: sigmoid(g); or, for the
+    silu gate mode the section mentions, silu(g) = g * sigmoid(g)."""
+    if gate_act == "sigmoid":
+        return sigmoid(g)
+    if gate_act == "silu":
+        g = np.asarray(g, dtype=np.float64)
+        return g * sigmoid(g)
+    raise ValueError(f"unknown gate activation {gate_act!r}")
+
+
 # --------------------------------------------------------------------------
 # RoPE  [SPARK §4 table and text; PROPE §13.3]
 # --------------------------------------------------------------------------
@@ -197,12 +214,13 @@ def linear_slot_positions(next_pos: int, capacity: int) -> np.ndarray:
 # --------------------------------------------------------------------------
 # attention  [SPARK §3 Eq. 1]
 # --------------------------------------------------------------------------
-def attend(q_rot, keys, values, ok, gate_logit) -> np.ndarray:
+def attend(q_rot, keys, values, ok, gate_logit, gate_act="sigmoid") -> np.ndarray:
     """Gated softmax attention of query rows against one kv-head's keys.
 
     q_rot: [M, D] rotated queries, keys/values: [N, D], ok: [M, N] visibility,
     gate_logit: [M]. Returns [M, D] fp64:
-      softmax(q k^T / sqrt(D) over visible keys) V * sigmoid(g)   (Eq. 1).
+      softmax(q k^T / sqrt(D) over visible keys) V * sigmoid(g)   (Eq. 1),
+    with silu(g) in place of sigmoid(g) for gate_act="silu".
     """
     q_rot = f64(q_rot)
     keys = f64(keys)
@@ -216,12 +234,12 @@ def attend(q_rot, keys, values, ok, gate_logit) -> np.ndarray:
     e = np.exp(s)
     a = e / e.sum(axis=1, keepdims=True)
     o = a @ values
-    return o * sigmoid(gate_logit)[:, None]
+    return o * gate_factor(gate_logit, gate_act)[:, None]
 
 
 def prefill_ref(q, k, v, gate, start_pos, *, window, theta, rotary_fraction,
                 hist_k=None, hist_v=None, hist_pos=None, rows=None,
-                round_keys=True):
+                round_keys=True, gate_act="sigmoid"):
     """One prefill call: S new tokens per sequence at positions
     start_pos[b] + 0..S-1, attending to the cached history plus themselves.
 
@@ -231,6 +249,7 @@ def prefill_ref(q, k, v, gate, start_pos, *, window, theta, rotary_fraction,
     rows: optional sorted indices into S; only those query rows are computed.
     round_keys: store the rotated new keys as bf16 before use (the cache
     holds bf16, [SPARK §1 dtype, §6]); False gives the pure fp64 variant.
+    gate_act: "sigmoid" (Eq. 1) or "silu" (the alternative gate mode).
 
     Returns (out [B, len(rows), Hq, D] fp64, k_hat [B, S, Hkv, D] fp64):
     k_hat is what the call writes to the cache for the new keys.
@@ -266,12 +285,12 @@ def prefill_ref(q, k, v, gate, start_pos, *, window, theta, rotary_fraction,
                 vals = np.concatenate([f64(hist_v[b, g]), vals])
             for h in range(g * G, (g + 1) * G):
                 out[b, :, h] = attend(q_rot[rows, h], keys, vals, ok,
-                                      gate[b, rows, h])
+                                      gate[b, rows, h], gate_act)
     return out, k_hat_all
 
 
 def decode_ref(q, k, v, gate, pos, cache_k, cache_v, *, kind, window, theta,
-               rotary_fraction, round_keys=True):
+               rotary_fraction, round_keys=True, gate_act="sigmoid"):
     """One decode step: one new token per sequence at position pos[b].
 
     q: [B, Hq, D], k/v: [B, Hkv, D], gate: [B, Hq]; cache_k/cache_v:
@@ -323,7 +342,7 @@ def decode_ref(q, k, v, gate, pos, cache_k, cache_v, *, kind, window, theta,
             for h in range(g * G, (g + 1) * G):
                 out[b, h] = attend(q_rot[h][None], keys, vals,
                                    np.ones((1, len(idx)), bool),
-                                   gate[b, h:h + 1])[0]
+                                   gate[b, h:h + 1], gate_act)[0]
     return out, slots, k_hats
 
 

@@ -50,6 +50,9 @@ def test_layer_defaults_match_page_tables():
     assert f_.window <= 0
     assert (f_.rope_theta, f_.rotary_fraction, f_.head_dim) == (
         t["rope"]["full"]["rope_theta"], t["rope"]["full"]["partial_rotary_factor"], 256)
+    assert s.gate_act == f_.gate_act == hb.GATE_SIGMOID       # Eq. 1 and both checkpoints
+    assert hb.layer_desc("full", gate_act="silu").gate_act == hb.GATE_SILU
+    assert ctypes.sizeof(hb.LayerDesc) == 40                  # the C struct's size
 
 
 def _prefill(L, desc, cache, B=1, S=8, start=(0,), ws_bytes=1 << 30, q=FAKE, ws=FAKE, gate=FAKE):
@@ -77,6 +80,8 @@ def test_prefill_rejects_bad_arguments(L):
     d = hb.layer_desc("sliding"); d.rope_theta = -1.0; cases.append((d, ring, {}, -4))
     d = hb.layer_desc("sliding"); d.window = 0; cases.append((d, ring, {}, -5))
     d = hb.layer_desc("full"); d.window = 512; cases.append((d, lin, {}, -5))
+    d = hb.layer_desc("full"); d.gate_act = 2; cases.append((d, lin, {}, -3))            # unknown gate mode
+    d = hb.layer_desc("full"); d.gate_act = -1; cases.append((d, lin, {}, -3))
     cases.append((fu, ring, {}, -6))                                                   # ring on a full layer
     cases.append((sl, hb.KvCacheC(FAKE, FAKE, hb.KV_RING, 1, 256), {}, -6))              # ring cap != window
     cases.append((sl, hb.KvCacheC(FAKE, FAKE, hb.KV_RING, 2, 512), {}, -6))              # batch mismatch
@@ -107,6 +112,7 @@ def test_decode_rejects_bad_arguments(L):
     assert _decode(L, fu, lin, pos=FAKE + 2) == -9
     assert _decode(L, fu, lin, pos=0) == -1
     assert _decode(L, sl, hb.KvCacheC(FAKE, FAKE, hb.KV_RING, 1, 100)) == -6
+    assert _decode(L, hb.layer_desc("full", gate_act=3), lin) == -3
     big = hb.KvCacheC(FAKE, FAKE, hb.KV_LINEAR, 1, 1 << 20)
     assert _decode(L, fu, big, max_pos=(1 << 20) - 1, ws_bytes=100) == -8
 

@@ -41,6 +41,20 @@ def check(tag, gpu, ref, max_abs=MAX_ABS, rel_rms=REL_RMS):
     assert ea <= max_abs and er <= rel_rms, (tag, ea, er)
 
 
+def check_silu(tag, gpu, ref, gate):
+    """The silu gate multiplies the sigmoid-gated output by g (silu(g) =
+    g * sigmoid(g)), so outputs reach |g| times the sigmoid case's size and
+    their bf16 rounding alone exceeds 1e-2 there. The max-abs bar is scaled
+    per (token, head) by max(1, |g|); the relative RMS bar is unchanged."""
+    assert torch.isfinite(gpu.float()).all(), f"{tag}: non-finite output"
+    d = O.f64(gpu.float().cpu()) - ref
+    scale = np.maximum(1.0, np.abs(O.f64(gate)))[..., None]
+    ea = float(np.abs(d / scale).max())
+    er = float(np.linalg.norm(d) / np.linalg.norm(ref))
+    log(f"[parity] {tag}: max_abs/max(1,|g|)={ea:.3e} rel_rms={er:.3e} max|ref|={np.abs(ref).max():.3f}")
+    assert ea <= MAX_ABS and er <= REL_RMS, (tag, ea, er)
+
+
 def check_bf16_values(tag, gpu_bf16, ref64, max_frac=1e-5):
     """Cached rotated keys: bf16 bits vs the oracle's bf16-rounded values."""
     g = O.f64(gpu_bf16.float().cpu())
@@ -101,8 +115,10 @@ def test_rope_apply_matches_oracle(layer):
 
 # ------------------------------------------------------------------ prefill
 def run_prefill(layer, B, S, Hq, Hkv, start, seed, cache_kind, cap, hist_seed=None, q_scale=1.0,
-                window=None):
-    overrides = {} if window is None else {"window": window}
+                window=None, gate_act="sigmoid"):
+    overrides = {"gate_act": gate_act}
+    if window is not None:
+        overrides["window"] = window
     desc = hb.layer_desc(layer, Hq, Hkv, **overrides)
     inp = synth.prefill_inputs(B, S, Hq, Hkv, seed=seed, q_scale=q_scale)
     if hist_seed is not None:
@@ -136,7 +152,8 @@ def oracle_prefill(desc, inp, ck, cv, start, kind, cap, rows=None):
     w = desc.window if desc.window > 0 else None
     hk, hv, hp = history_for(kind, ck, cv, start, cap)
     return O.prefill_ref(inp["q"], inp["k"], inp["v"], inp["gate"], start, window=w, theta=desc.rope_theta,
-                         rotary_fraction=desc.rotary_fraction, hist_k=hk, hist_v=hv, hist_pos=hp, rows=rows)
+                         rotary_fraction=desc.rotary_fraction, hist_k=hk, hist_v=hv, hist_pos=hp, rows=rows,
+                         gate_act=O.GATE_ACTS[desc.gate_act])
 
 
 def test_prefill_sliding_seq1024():
@@ -247,8 +264,11 @@ def test_chunked_prefill_equals_monolithic():
 
 
 # ------------------------------------------------------------------ decode
-def run_decode(layer, B, Hq, Hkv, pos, cap, kind, seed, hist_seed, window=None, fill=None):
-    overrides = {} if window is None else {"window": window}
+def run_decode(layer, B, Hq, Hkv, pos, cap, kind, seed, hist_seed, window=None, fill=None,
+               gate_act="sigmoid"):
+    overrides = {"gate_act": gate_act}
+    if window is not None:
+        overrides["window"] = window
     desc = hb.layer_desc(layer, Hq, Hkv, **overrides)
     inp = synth.decode_inputs(B, Hq, Hkv, seed=seed)
     ck = synth.cache_tensor(B, Hkv, cap, seed=hist_seed, fill_tokens=fill)
@@ -264,7 +284,8 @@ def run_decode(layer, B, Hq, Hkv, pos, cap, kind, seed, hist_seed, window=None, 
 def oracle_decode(desc, inp, ck, cv, pos, kind):
     w = desc.window if desc.window > 0 else None
     return O.decode_ref(inp["q"], inp["k"], inp["v"], inp["gate"], pos, ck, cv, kind=kind, window=w,
-                        theta=desc.rope_theta, rotary_fraction=desc.rotary_fraction)
+                        theta=desc.rope_theta, rotary_fraction=desc.rotary_fraction,
+                        gate_act=O.GATE_ACTS[desc.gate_act])
 
 
 def check_decode_cache(cache, inp, slots, k_hat):
@@ -313,6 +334,29 @@ def test_decode_partial_ring_and_small_cases():
     ref, slots, k_hat = oracle_decode(desc, inp, ck, cv, pos, "linear")
     check("decode full 8/2 ragged", out.cpu(), ref)
     check_decode_cache(cache, inp, slots, k_hat)
+
+
+def test_silu_gate_mode_prefill_and_decode():
+    # the alternative gate activation silu(g) = g * sigmoid(g) (page §3)
+    desc, inp, ck, cv, cache, out = run_prefill("sliding", 2, 300, 16, 4, [700, 0], 6, "ring", 512,
+                                                hist_seed=60, gate_act="silu")
+    ref, _ = oracle_prefill(desc, inp, ck, cv, [700, 0], "ring", 512)
+    check_silu("prefill sliding silu gate", out.cpu(), ref, inp["gate"])
+    desc, inp, ck, cv, cache, out = run_prefill("full", 1, 200, 16, 4, [1000], 7, "linear", 1200,
+                                                hist_seed=62, gate_act="silu")
+    ref, _ = oracle_prefill(desc, inp, ck, cv, [1000], "linear", 1200)
+    check_silu("prefill full silu gate", out.cpu(), ref, inp["gate"])
+    # decode: 256 (sequence, KV head) pairs finish in one workgroup each;
+    # one long sequence goes through the cross-workgroup merge
+    pos = synth.positions_uniform(64, 512, 1 << 20, seed=8).numpy()
+    desc, inp, ck, cv, cache, out, pos = run_decode("sliding", 64, 16, 4, pos, 512, "ring", 9, 64,
+                                                    gate_act="silu")
+    ref, _, _ = oracle_decode(desc, inp, ck, cv, pos, "ring")
+    check_silu("decode ring silu gate", out.cpu(), ref, inp["gate"])
+    desc, inp, ck, cv, cache, out, pos = run_decode("full", 1, 16, 4, [20000], 20001, "linear", 10, 66,
+                                                    fill=20000, gate_act="silu")
+    ref, _, _ = oracle_decode(desc, inp, ck, cv, pos, "linear")
+    check_silu("decode linear silu gate (merged splits)", out.cpu(), ref, inp["gate"])
 
 
 def test_ring_decode_equals_windowed_linear_decode():

@@ -235,6 +235,51 @@ def test_gate_closed_forms():
     np.testing.assert_allclose(ratio, np.broadcast_to(O.sigmoid(x["gate"])[..., None], ratio.shape), rtol=1e-12)
 
 
+def test_silu_gate_closed_forms_and_library_routine():
+    # the silu gate mode [SPARK §3]: silu(g) = g * sigmoid(g) in place of sigmoid(g)
+    x = _small_prefill(S=16, seed=5)
+    def run(gv, act):
+        g = np.full_like(x["gate"], gv)
+        return O.prefill_ref(x["q"], x["k"], x["v"], g, [0], window=None, theta=1e4,
+                             rotary_fraction=1.0, gate_act=act)[0]
+    o_one = run(40.0, "sigmoid")                        # sigmoid(40) == 1.0: ungated
+    assert np.array_equal(run(0.0, "silu"), np.zeros_like(o_one))   # silu(0) = 0
+    assert np.array_equal(run(40.0, "silu"), 40.0 * o_one)          # silu(40) = 40
+    np.testing.assert_allclose(run(math.log(3.0), "silu"), 0.75 * math.log(3.0) * o_one,
+                               rtol=1e-14, atol=1e-16)
+    # per (token, head) the silu output is g times the sigmoid output
+    kw = dict(window=None, theta=1e4, rotary_fraction=1.0)
+    o_sig = O.prefill_ref(x["q"], x["k"], x["v"], x["gate"], [0], **kw)[0]
+    o_silu = O.prefill_ref(x["q"], x["k"], x["v"], x["gate"], [0], gate_act="silu", **kw)[0]
+    np.testing.assert_allclose(o_silu, o_sig * O.f64(x["gate"])[..., None], rtol=1e-13, atol=1e-15)
+    # the gate factor itself against torch's silu in fp64, tails included
+    g = np.concatenate([np.linspace(-60.0, 60.0, 2001), [-1e-300, 0.0, 1e-300]])
+    want = torch.nn.functional.silu(torch.from_numpy(g)).numpy()
+    np.testing.assert_allclose(O.gate_factor(g, "silu"), want, rtol=1e-15, atol=1e-300)
+    with pytest.raises(ValueError):
+        O.gate_factor(g, "gelu")
+
+
+def test_silu_gate_in_decode_equals_prefill_row():
+    # a decode step with the silu gate equals the matching prefill row
+    rng = np.random.default_rng(11)
+    S, Hq, Hkv, D = 9, 4, 1, 256
+    q = rng.standard_normal((1, S, Hq, D))
+    k = O.bf16_rne(rng.standard_normal((1, S, Hkv, D)))
+    v = O.bf16_rne(rng.standard_normal((1, S, Hkv, D)))
+    g = 2.0 * rng.standard_normal((1, S, Hq))
+    kw = dict(window=None, theta=5e6, rotary_fraction=0.25, gate_act="silu")
+    pre, k_hat = O.prefill_ref(q, k, v, g, [0], **kw)
+    cap = 16
+    ck = np.zeros((1, Hkv, cap, D))
+    cv = np.zeros((1, Hkv, cap, D))
+    ck[0, :, :S - 1] = k_hat[0, :S - 1].transpose(1, 0, 2)
+    cv[0, :, :S - 1] = v[0, :S - 1].transpose(1, 0, 2)
+    dec, _, _ = O.decode_ref(q[:, S - 1], k[:, S - 1], v[:, S - 1], g[:, S - 1], [S - 1], ck, cv,
+                             kind="linear", **kw)
+    np.testing.assert_allclose(dec[0], pre[0, S - 1], rtol=1e-12, atol=1e-14)
+
+
 def test_new_keys_are_cached_as_bf16():
     x = _small_prefill(S=12, seed=6)
     _, kh = O.prefill_ref(x["q"], x["k"], x["v"], x["gate"], [77], window=None, theta=5e6, rotary_fraction=0.25)
