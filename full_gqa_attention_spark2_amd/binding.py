@@ -51,6 +51,20 @@ class KvCacheC(ctypes.Structure):
     ]
 
 
+class KvLayerPlan(ctypes.Structure):
+    _fields_ = [
+        ("layer_type", ctypes.c_int32),
+        ("kind", ctypes.c_int32),
+        ("capacity", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("k_offset", ctypes.c_uint64),
+        ("v_offset", ctypes.c_uint64),
+        ("bytes", ctypes.c_uint64),
+    ]
+
+
 _lib = None
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
@@ -64,6 +78,9 @@ _SIGS = {
     "hattn_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc), ctypes.POINTER(KvCacheC), _I]),
     "hattn_decode": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _I, _P, _I,
                                     ctypes.POINTER(KvCacheC), _P, _P, ctypes.c_size_t, _P]),
+    "hattn_kv_plan": (ctypes.c_int, [_I, _P, _I, _I, _I, _I, ctypes.POINTER(KvLayerPlan),
+                                     ctypes.POINTER(ctypes.c_uint64)]),
+    "hattn_kv_cache_at": (ctypes.c_int, [ctypes.POINTER(KvLayerPlan), _P, ctypes.POINTER(KvCacheC)]),
     "hattn_debug_index_probe": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _I, _I, _I, _I, _P, _P, _P, _P]),
     "hattn_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "hattn_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]),
@@ -226,6 +243,46 @@ def hattn_decode(desc, q, k, v, gate, pos, max_pos, cache, out=None, workspace=N
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), B, _ptr(pos), int(max_pos),
         ctypes.byref(cc), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(q.device)))
     return out
+
+
+def hattn_kv_plan(n_layers, num_kv_heads, batch, max_tokens, window=512, layer_types=None):
+    """Cache layout of a layer stack in one arena: (list of KvLayerPlan,
+    arena bytes). layer_types: None (full iff i mod 4 == 3) or a sequence of
+    "sliding"/"full" (or 0/1)."""
+    plan = (KvLayerPlan * n_layers)()
+    total = ctypes.c_uint64()
+    lt = None
+    if layer_types is not None:
+        if len(layer_types) != n_layers:
+            raise ValueError("layer_types must have n_layers entries")
+        lt = (ctypes.c_int32 * n_layers)(*[{"sliding": LAYER_SLIDING, "full": LAYER_FULL}.get(t, t)
+                                          for t in layer_types])
+    _check("hattn_kv_plan", lib().hattn_kv_plan(n_layers, ctypes.cast(lt, ctypes.c_void_p) if lt else None,
+                                                num_kv_heads, batch, max_tokens, window, plan,
+                                                ctypes.byref(total)))
+    return list(plan), int(total.value)
+
+
+def kv_arena(arena_bytes, device="cuda"):
+    """A device arena of the planned size (uint8, 256-byte aligned)."""
+    return torch.empty(max(int(arena_bytes), 256), dtype=torch.uint8, device=device)
+
+
+def kv_cache_at(layer_plan, arena):
+    """The KVCache of one planned layer: K and V are bf16 views into the
+    arena at the offsets hattn_kv_cache_at returns."""
+    _need(arena, "arena", torch.uint8)
+    cc = KvCacheC()
+    _check("hattn_kv_cache_at", lib().hattn_kv_cache_at(ctypes.byref(layer_plan), _ptr(arena), ctypes.byref(cc)))
+    shape = (cc.batch, layer_plan.num_kv_heads, cc.capacity, HEAD_DIM)
+    n = cc.batch * layer_plan.num_kv_heads * cc.capacity * HEAD_DIM * 2
+    base = arena.data_ptr()
+    def view(ptr):
+        off = ptr - base
+        if off < 0 or off + n > arena.numel():
+            raise ValueError("planned block lies outside the arena")
+        return arena[off:off + n].view(torch.bfloat16).view(shape)
+    return KVCache(view(cc.k), view(cc.v), cc.kind)
 
 
 def hattn_debug_index_probe(desc, kind, capacity, q_pos0, n_q, device="cuda"):

@@ -161,6 +161,54 @@ int hattn_decode(const hattn_layer_desc* desc, const void* q, const void* k,
                  const hattn_kv_cache* cache, void* out, void* workspace,
                  size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * KV planner (page §6 参数与 KV Cache 估算, KV table: K and V of every KV
+ * head in bf16, 2 * num_kv_heads * 256 * 2 bytes per token and layer; full
+ * layers keep every token, sliding layers at most the window; §2: layer i
+ * (counting from 0) is a full layer iff i mod 4 == 3).
+ *
+ * hattn_kv_plan lays out the caches of a whole layer stack in one arena:
+ *   layer_types: int32 [n_layers] hattn_layer_type, HOST memory, or NULL
+ *     for the page's schedule (full iff i mod 4 == 3).
+ *   batch: sequences; max_tokens: the largest context (positions
+ *     0 .. max_tokens-1) any sequence will reach, 1 .. 2^30.
+ *   window: the sliding layers' window (512 on the page), >= 1.
+ *   plan: HOST array of n_layers entries, filled in.
+ *   arena_bytes: receives the arena size the plan needs.
+ * A full layer gets a linear cache of capacity max_tokens. A sliding layer
+ * gets a ring of capacity == window when max_tokens > window, else a linear
+ * cache of capacity max_tokens (the same visible set, no slot ever reused),
+ * so its size is min(max_tokens, window) tokens, as on the page's table.
+ * Every K and V block starts on a 256-byte boundary; blocks follow layer
+ * order, K before V. Pure host arithmetic: nothing is allocated or enqueued.
+ * Errors: HATTN_ERR_NULL (plan or arena_bytes NULL), HATTN_ERR_SHAPE
+ * (n_layers, batch, num_kv_heads or max_tokens out of range, an unknown
+ * layer type), HATTN_ERR_WINDOW (window < 1). */
+typedef struct {
+  int32_t layer_type;  /* hattn_layer_type                                    */
+  int32_t kind;        /* hattn_kv_kind                                       */
+  int32_t capacity;    /* slots per (sequence, kv head)                       */
+  int32_t num_kv_heads;
+  int32_t batch;       /* sequences                                           */
+  int32_t reserved;    /* 0                                                   */
+  uint64_t k_offset;   /* byte offset of the K block in the arena             */
+  uint64_t v_offset;   /* byte offset of the V block                          */
+  uint64_t bytes;      /* K + V bytes of the layer (padding excluded)         */
+} hattn_kv_layer_plan;
+
+int hattn_kv_plan(int32_t n_layers, const int32_t* layer_types,
+                  int32_t num_kv_heads, int32_t batch, int32_t max_tokens,
+                  int32_t window, hattn_kv_layer_plan* plan,
+                  uint64_t* arena_bytes);
+
+/* The cache descriptor of one planned layer inside an arena (device memory
+ * of at least arena_bytes, 256-byte aligned, owned by the caller): k and v
+ * point at arena + the layer's offsets. Errors: HATTN_ERR_NULL,
+ * HATTN_ERR_ALIGN (arena not 256-byte aligned), HATTN_ERR_SHAPE (an
+ * inconsistent plan entry). */
+int hattn_kv_cache_at(const hattn_kv_layer_plan* layer, void* arena,
+                      hattn_kv_cache* out);
+
 /* Profiling hook for benchmarks. While enabled, every hattn_prefill records
  * a HIP event pair around its attention kernel (HATTN_PROFILE_PREFILL) and
  * every hattn_decode around its attention and merge kernels

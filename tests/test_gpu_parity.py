@@ -34,11 +34,27 @@ def errors(gpu, ref):
     return float(np.abs(d).max()), float(np.linalg.norm(d) / np.linalg.norm(ref))
 
 
-def check(tag, gpu, ref, max_abs=MAX_ABS, rel_rms=REL_RMS):
+def store_allowance(ref):
+    """What the bf16 store alone may add to an element's error beyond its
+    size at |ref| < 2: half a bf16 ulp of |ref| minus 2^-8 (the half ulp on
+    [1, 2)), 0 below 2. Outputs this large only occur in rows that see a
+    handful of keys (the first prefill rows, tiny windows)."""
+    a = np.abs(ref)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return np.maximum(0.0, 2.0 ** (e - 8) - 2.0 ** -8)
+
+
+def check(tag, gpu, ref, max_abs=MAX_ABS, rel_rms=REL_RMS, strict=False):
+    """Max-abs and relative-RMS bars. strict: the plain max-abs bar (the
+    headline workloads); otherwise each element's bar is widened by what
+    the bf16 store alone adds at its magnitude (store_allowance)."""
     assert torch.isfinite(gpu.float()).all(), f"{tag}: non-finite output"
     ea, er = errors(gpu, ref)
-    log(f"[parity] {tag}: max_abs={ea:.3e} rel_rms={er:.3e} max|ref|={np.abs(ref).max():.3f}")
-    assert ea <= max_abs and er <= rel_rms, (tag, ea, er)
+    d = np.abs(O.f64(gpu.float().cpu()) - ref)
+    eq = float((d - store_allowance(ref)).max())
+    log(f"[parity] {tag}: max_abs={ea:.3e} (beyond the store's extra rounding {eq:.3e}) "
+        f"rel_rms={er:.3e} max|ref|={np.abs(ref).max():.3f}")
+    assert (ea if strict else eq) <= max_abs and er <= rel_rms, (tag, ea, eq, er)
 
 
 def check_silu(tag, gpu, ref, gate):
@@ -156,11 +172,28 @@ def oracle_prefill(desc, inp, ck, cv, start, kind, cap, rows=None):
                          gate_act=O.GATE_ACTS[desc.gate_act])
 
 
+def cache_after_prefill(ck, cv, k_hat, v, start, kind, cap):
+    """The oracle's view of a cache after a prefill: the history ck/cv with
+    the new tokens' oracle keys k_hat [B,S,Hkv,D] and values v at their slots
+    (position p in slot p, or p mod cap for a ring's last cap tokens)."""
+    hk, hv = O.f64(ck).copy(), O.f64(cv).copy()
+    B, S = k_hat.shape[:2]
+    vv = O.f64(v)
+    for b in range(B):
+        keep = min(S, cap) if kind == "ring" else S
+        for i in range(S - keep, S):
+            p = start[b] + i
+            slot = p % cap if kind == "ring" else p
+            hk[b, :, slot] = k_hat[b, i]
+            hv[b, :, slot] = vv[b, i]
+    return hk, hv
+
+
 def test_prefill_sliding_seq1024():
     # one sliding layer: B=1, S=1024, 16/4 heads, theta 1e4 over 256 channels, window 512, seed 0
     desc, inp, ck, cv, cache, out = run_prefill("sliding", 1, 1024, 16, 4, [0], 0, "ring", 512)
     ref, k_hat = oracle_prefill(desc, inp, ck, cv, [0], "ring", 512)
-    check("prefill sliding S=1024", out.cpu(), ref)
+    check("prefill sliding S=1024", out.cpu(), ref, strict=True)
     # the ring keeps positions 512..1023 at slots p mod 512
     slots = np.arange(512, 1024) % 512
     check_bf16_values("ring keys after prefill", cache.k[0, :, slots].cpu().permute(1, 0, 2),
@@ -181,7 +214,7 @@ def test_prefill_full_seq8192_sampled():
     rng = np.random.default_rng(5)
     rows = np.unique(np.concatenate([np.arange(32), np.arange(S - 32, S), rng.integers(0, S, 64)]))
     ref, k_hat = oracle_prefill(desc, inp, ck, cv, [0], "linear", S, rows=rows)
-    check("prefill full S=8192 (sampled rows)", out[:, rows].cpu(), ref)
+    check("prefill full S=8192 (sampled rows)", out[:, rows].cpu(), ref, strict=True)
     check_bf16_values("linear keys after prefill", cache.k[0].cpu().permute(1, 0, 2), k_hat[0])
     assert torch.equal(cache.v[0].cpu().permute(1, 0, 2), inp["v"][0])
 
@@ -224,7 +257,7 @@ def test_prefill_and_decode_other_rotary_widths(fraction):
     # decode of the next token on the same cache
     dinp = synth.decode_inputs(B, 16, 4, seed=42)
     pos = np.array([S, S + 5])
-    hk, hv = cache.k.cpu(), cache.v.cpu()
+    hk, hv = cache_after_prefill(ck, cv, k_hat, inp["v"], [0, 5], "linear", 128)
     dd = to_dev(dinp)
     o = hb.hattn_decode(desc, dd["q"], dd["k"], dd["v"], dd["gate"], torch.as_tensor(pos, dtype=torch.int32).to(DEV),
                         int(pos.max()), cache)
@@ -300,7 +333,7 @@ def test_decode_sliding_batch64_ring():
     pos = synth.positions_uniform(64, 512, 1 << 20, seed=0).numpy()
     desc, inp, ck, cv, cache, out, pos = run_decode("sliding", 64, 16, 4, pos, 512, "ring", 0, 100)
     ref, slots, k_hat = oracle_decode(desc, inp, ck, cv, pos, "ring")
-    check("decode sliding B=64 ring", out.cpu(), ref)
+    check("decode sliding B=64 ring", out.cpu(), ref, strict=True)
     check_decode_cache(cache, inp, slots, k_hat)
 
 
@@ -309,7 +342,7 @@ def test_decode_full_1m_tokens():
     n = 1 << 20
     desc, inp, ck, cv, cache, out, pos = run_decode("full", 1, 16, 4, [n - 1], n, "linear", 1, 200, fill=n - 1)
     ref, slots, k_hat = oracle_decode(desc, inp, ck, cv, pos, "linear")
-    check("decode full B=1 L=2^20", out.cpu(), ref)
+    check("decode full B=1 L=2^20", out.cpu(), ref, strict=True)
     check_decode_cache(cache, inp, slots, k_hat)
 
 
@@ -317,7 +350,7 @@ def test_decode_full_batch8_131072():
     n = 131072
     desc, inp, ck, cv, cache, out, pos = run_decode("full", 8, 16, 4, [n - 1] * 8, n, "linear", 2, 300, fill=n - 1)
     ref, slots, k_hat = oracle_decode(desc, inp, ck, cv, pos, "linear")
-    check("decode full B=8 L=131072", out.cpu(), ref)
+    check("decode full B=8 L=131072", out.cpu(), ref, strict=True)
     check_decode_cache(cache, inp, slots, k_hat)
 
 
@@ -357,6 +390,46 @@ def test_silu_gate_mode_prefill_and_decode():
                                                     fill=20000, gate_act="silu")
     ref, _, _ = oracle_decode(desc, inp, ck, cv, pos, "linear")
     check_silu("decode linear silu gate (merged splits)", out.cpu(), ref, inp["gate"])
+
+
+def test_planned_arena_layer_stack():
+    # a 4-layer stack (3 sliding, 1 full; page §2 order) planned into one
+    # arena by hattn_kv_plan; two prefill chunks and a decode step per layer
+    B, T, S1, S2 = 2, 700, 400, 200
+    plan, total = hb.hattn_kv_plan(4, 4, B, T)
+    arena = hb.kv_arena(total)
+    arena.fill_(0xFF)                      # every bf16 reads as NaN until written
+    caches = [hb.kv_cache_at(e, arena) for e in plan]
+    assert [c.kind for c in caches] == [hb.KV_RING] * 3 + [hb.KV_LINEAR]
+    for li in (2, 3):
+        desc = hb.layer_desc("full" if li == 3 else "sliding")
+        kind = "linear" if li == 3 else "ring"
+        cap = plan[li].capacity
+        others = [(arena[e.k_offset:e.k_offset + e.bytes // 2].clone(), e) for j, e in enumerate(plan) if j != li]
+        inp = synth.prefill_inputs(B, S1 + S2, 16, 4, seed=70 + li)
+        d = to_dev(inp)
+        sl = lambda t, a, b: t[:, a:b].contiguous()
+        o1 = hb.hattn_prefill(desc, *(sl(d[x], 0, S1) for x in ("q", "k", "v", "gate")), [0, 0], caches[li])
+        o2 = hb.hattn_prefill(desc, *(sl(d[x], S1, S1 + S2) for x in ("q", "k", "v", "gate")), [S1, S1],
+                              caches[li])
+        torch.cuda.synchronize()
+        # the oracle's monolithic prefill of all S1 + S2 tokens (chunked == monolithic)
+        ck = torch.zeros((B, 4, cap, 256), dtype=torch.bfloat16)
+        ref, k_hat = oracle_prefill(desc, inp, ck, ck.clone(), [0, 0], kind, cap)
+        check(f"arena layer {li} prefill", torch.cat([o1, o2], 1).cpu(), ref)
+        # decode of token S1 + S2 on the arena cache
+        dinp = synth.decode_inputs(B, 16, 4, seed=80 + li)
+        pos = np.array([S1 + S2] * B)
+        dd = to_dev(dinp)
+        o = hb.hattn_decode(desc, dd["q"], dd["k"], dd["v"], dd["gate"],
+                            torch.as_tensor(pos, dtype=torch.int32).to(DEV), S1 + S2, caches[li])
+        torch.cuda.synchronize()
+        hk, hv = cache_after_prefill(ck, ck.clone(), k_hat, inp["v"], [0, 0], kind, cap)
+        ref_d, _, _ = oracle_decode(desc, dinp, hk, hv, pos, kind)
+        check(f"arena layer {li} decode", o.cpu(), ref_d)
+        # the other layers' K blocks are untouched
+        for before, e in others:
+            assert torch.equal(arena[e.k_offset:e.k_offset + e.bytes // 2], before)
 
 
 def test_ring_decode_equals_windowed_linear_decode():
@@ -540,4 +613,4 @@ def test_chunked_prefill_1p7b_shape_sampled(layer):
     rng = np.random.default_rng(3)
     rows = np.unique(np.concatenate([np.arange(64), rng.integers(0, S, 64)]))
     ref, k_hat = oracle_prefill(desc, inp, ck, cv, [s0, s0], kind, cap, rows=rows)
-    check(f"chunked prefill 1.7B {layer} (sampled rows)", out[:, rows].cpu(), ref)
+    check(f"chunked prefill 1.7B {layer} (sampled rows)", out[:, rows].cpu(), ref, strict=True)
