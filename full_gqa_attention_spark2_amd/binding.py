@@ -75,6 +75,10 @@ _SIGS = {
     "hattn_prefill_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc), ctypes.POINTER(KvCacheC), _I, _I]),
     "hattn_prefill": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _I, _I, _P,
                                      ctypes.POINTER(KvCacheC), _P, _P, ctypes.c_size_t, _P]),
+    "hattn_prefill_varlen_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc), ctypes.POINTER(KvCacheC),
+                                                              _I, _P]),
+    "hattn_prefill_varlen": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _I, _P, _P,
+                                            ctypes.POINTER(KvCacheC), _P, _P, ctypes.c_size_t, _P]),
     "hattn_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc), ctypes.POINTER(KvCacheC), _I]),
     "hattn_decode": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _I, _P, _I,
                                     ctypes.POINTER(KvCacheC), _P, _P, ctypes.c_size_t, _P]),
@@ -219,6 +223,36 @@ def hattn_prefill(desc, q, k, v, gate, start_pos, cache, out=None, workspace=Non
     ws = _workspace(prefill_workspace_size(desc, cache, B, S), q.device, workspace)
     _check("hattn_prefill", lib().hattn_prefill(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), B, S,
+        ctypes.cast(sp, ctypes.c_void_p), ctypes.byref(cc), _ptr(out), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(q.device)))
+    return out
+
+
+def hattn_prefill_varlen(desc, q, k, v, gate, cu_seqlens, start_pos, cache, out=None, workspace=None):
+    """Ragged prefill over packed tokens: q [T,Hq,256], k/v [T,Hkv,256],
+    gate [T,Hq]; host cu_seqlens [B+1] (sequence b = rows cu[b]..cu[b+1]-1)
+    and start positions [B]; writes the new keys/values to ``cache``;
+    returns out [T,Hq,256]."""
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    B = len(cu_seqlens) - 1
+    _need(q, "q")
+    _need(k, "k", shape=(T, Hkv, D))
+    _need(v, "v", shape=(T, Hkv, D))
+    _need(gate, "gate", shape=(T, Hq))
+    if int(cu_seqlens[-1]) != T or len(start_pos) != B:
+        raise ValueError("cu_seqlens[-1] must equal the packed token count and start_pos have B entries")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", shape=q.shape)
+    cu = (ctypes.c_int32 * (B + 1))(*[int(x) for x in cu_seqlens])
+    sp = (ctypes.c_int32 * B)(*[int(x) for x in start_pos])
+    cc = cache.c()
+    size = int(lib().hattn_prefill_varlen_workspace_size(ctypes.byref(desc), ctypes.byref(cc), B,
+                                                         ctypes.cast(cu, ctypes.c_void_p)))
+    ws = _workspace(size, q.device, workspace)
+    _check("hattn_prefill_varlen", lib().hattn_prefill_varlen(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), B, ctypes.cast(cu, ctypes.c_void_p),
         ctypes.cast(sp, ctypes.c_void_p), ctypes.byref(cc), _ptr(out), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(q.device)))
     return out

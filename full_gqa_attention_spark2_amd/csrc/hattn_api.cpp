@@ -117,12 +117,15 @@ struct PrefillLayout {
   size_t total;
 };
 
-PrefillLayout prefill_layout(const hattn_layer_desc* d, const hattn_kv_cache* c, int B, int S) {
+// total_tokens: packed new tokens of all sequences; max_len: the longest
+// sequence's new tokens.
+PrefillLayout prefill_layout(const hattn_layer_desc* d, const hattn_kv_cache* c, int B,
+                             long long total_tokens, int max_len) {
   PrefillLayout L{};
   const int r = rotary_channels(d->rotary_fraction, d->head_dim);
-  L.table_bytes = align_up((size_t)B * S * (r / 2) * 8, 256);
+  L.table_bytes = align_up((size_t)total_tokens * (r / 2) * 8, 256);
   if (c->kind == HATTN_KV_RING) {
-    L.stage_rows = (d->window - 1) + S;
+    L.stage_rows = (d->window - 1) + max_len;
     L.stage_bytes = align_up((size_t)B * d->num_kv_heads * L.stage_rows * d->head_dim * 2, 256);
   }
   L.total = L.table_bytes + 2 * L.stage_bytes;
@@ -230,35 +233,47 @@ int hattn_rope_apply(void* x, int32_t n_tok, int32_t n_heads, int32_t head_dim, 
 size_t hattn_prefill_workspace_size(const hattn_layer_desc* desc, const hattn_kv_cache* cache,
                                     int32_t batch, int32_t seq_len) {
   if (check_desc(desc) != HATTN_OK || !cache || batch <= 0 || seq_len < 0) return 0;
-  return prefill_layout(desc, cache, batch, seq_len).total;
+  return prefill_layout(desc, cache, batch, (long long)batch * seq_len, seq_len).total;
 }
 
-int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
-                  const void* gate, int32_t batch, int32_t seq_len, const int32_t* start_pos,
-                  const hattn_kv_cache* cache, void* out, void* workspace, size_t workspace_bytes,
-                  hipStream_t stream) {
-  int st = check_desc(desc);
-  if (st != HATTN_OK) return st;
-  if (batch <= 0 || seq_len < 0) return HATTN_ERR_SHAPE;
-  if (batch > kMaxPrefillBatch) return HATTN_ERR_UNSUPPORTED;
-  st = check_cache(desc, cache, batch);
-  if (st != HATTN_OK) return st;
-  if (!start_pos) return HATTN_ERR_NULL;
-  if (seq_len == 0) return HATTN_OK;
+size_t hattn_prefill_varlen_workspace_size(const hattn_layer_desc* desc, const hattn_kv_cache* cache,
+                                           int32_t batch, const int32_t* cu_seqlens) {
+  if (check_desc(desc) != HATTN_OK || !cache || batch <= 0 || !cu_seqlens || cu_seqlens[0] != 0) return 0;
+  int max_len = 0;
+  for (int b = 0; b < batch; ++b) {
+    const long long n = (long long)cu_seqlens[b + 1] - cu_seqlens[b];
+    if (n < 0) return 0;
+    max_len = std::max<int>(max_len, (int)n);
+  }
+  return prefill_layout(desc, cache, batch, cu_seqlens[batch], max_len).total;
+}
+
+namespace {
+
+// One prefill call over packed new tokens: sequence b's tokens are rows
+// tok0[b] .. tok0[b] + len[b] - 1 of q/k/v/gate/out, at positions
+// start_pos[b] + 0 .. len[b] - 1.
+int prefill_packed(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
+                   const void* gate, int32_t batch, const int* tok0, const int* len, long long total,
+                   const int32_t* start_pos, const hattn_kv_cache* cache, void* out, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  const bool ring = cache->kind == HATTN_KV_RING;
+  int max_len = 0;
+  for (int b = 0; b < batch; ++b) {
+    const long long s0 = start_pos[b];
+    if (s0 < 0 || s0 + len[b] > kMaxPos) return HATTN_ERR_POSITION;
+    if (!ring && s0 + len[b] > cache->capacity) return HATTN_ERR_CAPACITY;
+    max_len = std::max(max_len, len[b]);
+  }
+  if (total == 0) return HATTN_OK;
   if (!q || !k || !v || !gate || !out) return HATTN_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || ((uintptr_t)gate & 1u))
     return HATTN_ERR_ALIGN;
-  const bool ring = cache->kind == HATTN_KV_RING;
-  for (int b = 0; b < batch; ++b) {
-    const long long s0 = start_pos[b];
-    if (s0 < 0 || s0 + seq_len > kMaxPos) return HATTN_ERR_POSITION;
-    if (!ring && s0 + seq_len > cache->capacity) return HATTN_ERR_CAPACITY;
-  }
   // The attention kernel addresses a (sequence, KV head) slab of key rows
   // with 32-bit byte offsets (512 B per row).
-  const long long key_rows = ring ? (long long)desc->window - 1 + seq_len : (long long)cache->capacity;
+  const long long key_rows = ring ? (long long)desc->window - 1 + max_len : (long long)cache->capacity;
   if (key_rows > kMaxPrefillKeyRows) return HATTN_ERR_UNSUPPORTED;
-  const PrefillLayout L = prefill_layout(desc, cache, batch, seq_len);
+  const PrefillLayout L = prefill_layout(desc, cache, batch, total, max_len);
   if (!workspace || workspace_bytes < L.total) return HATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return HATTN_ERR_ALIGN;
 
@@ -282,7 +297,8 @@ int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k, co
     rc.cap = cache->capacity;
     rc.stage_rows = L.stage_rows;
     for (int b = 0; b < batch; ++b) {
-      const int hist = std::min(start_pos[b], w - 1);
+      // a sequence without new tokens needs no history
+      const int hist = len[b] > 0 ? std::min(start_pos[b], w - 1) : 0;
       rc.count[b] = hist;
       rc.first_pos[b] = start_pos[b] - hist;
       rc.stage_row0[b] = 0;
@@ -300,25 +316,29 @@ int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k, co
   ra.dst_k = ring ? stage_k : (uint16_t*)cache->k;
   ra.dst_v = ring ? stage_v : (uint16_t*)cache->v;
   ra.B = batch;
-  ra.S = seq_len;
+  ra.max_len = max_len;
   ra.Hkv = Hkv;
   ra.dst_rows = ring ? L.stage_rows : cache->capacity;
   ra.r = r;
-  // a ring keeps the last min(S, capacity) new tokens; the prep kernel
-  // writes them to their slots (the history it replaces is already staged)
+  // a ring keeps each sequence's last min(len, capacity) new tokens; the
+  // prep kernel writes them to their slots (the history they replace is
+  // already staged)
   ra.ring_k = ring ? (uint16_t*)cache->k : nullptr;
   ra.ring_v = ring ? (uint16_t*)cache->v : nullptr;
   ra.ring_cap = cache->capacity;
-  ra.ring_from = ring ? seq_len - std::min(seq_len, cache->capacity) : seq_len;
   fill_inv_freq(desc->rope_theta, r, ra.inv_freq);
   PrefillAttnArgs aa{};
   for (int b = 0; b < batch; ++b) {
     const int hist = ring ? std::min(start_pos[b], w - 1) : 0;
     ra.start[b] = start_pos[b];
     ra.dst_row0[b] = ring ? hist : start_pos[b];
+    ra.tok0[b] = tok0[b];
+    ra.len[b] = len[b];
     aa.start[b] = start_pos[b];
     aa.key_pos0[b] = ring ? start_pos[b] - hist : 0;
-    aa.n_keys[b] = ring ? hist + seq_len : start_pos[b] + seq_len;
+    aa.n_keys[b] = ring ? hist + len[b] : start_pos[b] + len[b];
+    aa.tok0[b] = tok0[b];
+    aa.len[b] = len[b];
   }
   hipError_t e = launch_prefill_prep(ra, stream);
   if (e != hipSuccess) return HATTN_ERR_LAUNCH;
@@ -331,20 +351,71 @@ int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k, co
   aa.gate = (const uint16_t*)gate;
   aa.out = (uint16_t*)out;
   aa.B = batch;
-  aa.S = seq_len;
   aa.Hq = Hq;
   aa.Hkv = Hkv;
   aa.rows = ring ? L.stage_rows : cache->capacity;
   aa.window = desc->layer_type == HATTN_LAYER_SLIDING ? w : 0;
   aa.r = r;
   aa.gate_act = desc->gate_act;
-  aa.q_tiles = (seq_len + kPrefillBlockQ - 1) / kPrefillBlockQ;
+  aa.q_tiles = (max_len + kPrefillBlockQ - 1) / kPrefillBlockQ;
   hipEvent_t prof = profile_begin(HATTN_PROFILE_PREFILL, stream);
   e = launch_prefill_attn(aa, stream);
   profile_end(prof, stream);
   if (e != hipSuccess) return HATTN_ERR_LAUNCH;
 
   return HATTN_OK;
+}
+
+// Checks shared by both prefill entry points (before any sequence data).
+int prefill_common_checks(const hattn_layer_desc* desc, const hattn_kv_cache* cache, int32_t batch,
+                          const int32_t* start_pos) {
+  int st = check_desc(desc);
+  if (st != HATTN_OK) return st;
+  if (batch <= 0) return HATTN_ERR_SHAPE;
+  if (batch > kMaxPrefillBatch) return HATTN_ERR_UNSUPPORTED;
+  st = check_cache(desc, cache, batch);
+  if (st != HATTN_OK) return st;
+  if (!start_pos) return HATTN_ERR_NULL;
+  return HATTN_OK;
+}
+
+}  // namespace
+
+int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
+                  const void* gate, int32_t batch, int32_t seq_len, const int32_t* start_pos,
+                  const hattn_kv_cache* cache, void* out, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+  int st = check_desc(desc);
+  if (st != HATTN_OK) return st;
+  if (batch <= 0 || seq_len < 0) return HATTN_ERR_SHAPE;
+  st = prefill_common_checks(desc, cache, batch, start_pos);
+  if (st != HATTN_OK) return st;
+  if ((long long)batch * seq_len > INT32_MAX) return HATTN_ERR_UNSUPPORTED;
+  int tok0[kMaxPrefillBatch], len[kMaxPrefillBatch];
+  for (int b = 0; b < batch; ++b) {
+    tok0[b] = b * seq_len;
+    len[b] = seq_len;
+  }
+  return prefill_packed(desc, q, k, v, gate, batch, tok0, len, (long long)batch * seq_len, start_pos,
+                        cache, out, workspace, workspace_bytes, stream);
+}
+
+int hattn_prefill_varlen(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
+                         const void* gate, int32_t batch, const int32_t* cu_seqlens,
+                         const int32_t* start_pos, const hattn_kv_cache* cache, void* out,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int st = prefill_common_checks(desc, cache, batch, start_pos);
+  if (st != HATTN_OK) return st;
+  if (!cu_seqlens) return HATTN_ERR_NULL;
+  if (cu_seqlens[0] != 0) return HATTN_ERR_SHAPE;
+  int tok0[kMaxPrefillBatch], len[kMaxPrefillBatch];
+  for (int b = 0; b < batch; ++b) {
+    if (cu_seqlens[b + 1] < cu_seqlens[b]) return HATTN_ERR_SHAPE;
+    tok0[b] = cu_seqlens[b];
+    len[b] = cu_seqlens[b + 1] - cu_seqlens[b];
+  }
+  return prefill_packed(desc, q, k, v, gate, batch, tok0, len, cu_seqlens[batch], start_pos, cache, out,
+                        workspace, workspace_bytes, stream);
 }
 
 size_t hattn_decode_workspace_size(const hattn_layer_desc* desc, const hattn_kv_cache* cache,

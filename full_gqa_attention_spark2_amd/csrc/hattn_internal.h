@@ -15,22 +15,25 @@ constexpr long long kMaxPrefillKeyRows = 1LL << 23;  // key rows per (sequence, 
 // Per new prefill token: cos/sin of its RoPE angles (fp32 table for the
 // attention kernel's query rotation) and its rotated key and value, written
 // as rows of dst (a cache or the staging buffer, [B][Hkv][rows][256]).
+// New tokens are packed: sequence b's token i is row tok0[b] + i of k, v
+// and the table, for i < len[b].
 struct PrefillPrepArgs {
-  const uint16_t* k;
+  const uint16_t* k;      // bf16 [T][Hkv][256]
   const uint16_t* v;
-  float2* table;    // [B][S][r/2] (cos, sin)
+  float2* table;          // [T][r/2] (cos, sin)
   uint16_t* dst_k;
   uint16_t* dst_v;
-  int B, S, Hkv;
+  int B, max_len, Hkv;
   int dst_rows;     // rows per (b, kv head) in dst
   int r;            // rotated channels
-  uint16_t* ring_k; // ring cache that also receives tokens >= ring_from (or null)
-  uint16_t* ring_v;
+  uint16_t* ring_k; // ring cache that also receives each sequence's last
+  uint16_t* ring_v; //   min(len, ring_cap) tokens (or null)
   int ring_cap;
-  int ring_from;
   double inv_freq[128];
   int start[kMaxPrefillBatch];    // position of token 0 of sequence b
   int dst_row0[kMaxPrefillBatch]; // dst row of token 0 of sequence b
+  int tok0[kMaxPrefillBatch];     // packed row of token 0 of sequence b
+  int len[kMaxPrefillBatch];      // new tokens of sequence b
 };
 
 // Copies between a ring cache and the linear staging buffer.
@@ -45,22 +48,25 @@ struct RingCopyArgs {
   int stage_row0[kMaxPrefillBatch];// staging row of the first copied row
 };
 
+// Queries are packed like the new tokens of PrefillPrepArgs.
 struct PrefillAttnArgs {
-  const uint16_t* q;      // bf16 [B][S][Hq][256], before RoPE
-  const float2* table;    // [B][S][r/2] cos/sin of the query positions
+  const uint16_t* q;      // bf16 [T][Hq][256], before RoPE
+  const float2* table;    // [T][r/2] cos/sin of the query positions
   const uint16_t* kc;     // bf16 [B][Hkv][rows][256], rotated keys
   const uint16_t* vc;
-  const uint16_t* gate;   // bf16 [B][S][Hq]
-  uint16_t* out;          // bf16 [B][S][Hq][256]
-  int B, S, Hq, Hkv;
+  const uint16_t* gate;   // bf16 [T][Hq]
+  uint16_t* out;          // bf16 [T][Hq][256]
+  int B, Hq, Hkv;
   int rows;               // rows per (b, kv head) in kc / vc
   int window;             // <= 0: unbounded
   int r;                  // rotated channels (multiple of 16)
-  int q_tiles;            // ceil(S / kPrefillBlockQ)
+  int q_tiles;            // ceil(max len / kPrefillBlockQ)
   int gate_act;           // 0 sigmoid, 1 silu
   int start[kMaxPrefillBatch];     // position of query 0
   int key_pos0[kMaxPrefillBatch];  // position held by key row 0
   int n_keys[kMaxPrefillBatch];    // valid key rows
+  int tok0[kMaxPrefillBatch];      // packed row of query 0
+  int len[kMaxPrefillBatch];       // queries of sequence b
 };
 
 struct DecodeArgs {
@@ -95,6 +101,13 @@ struct ProbeArgs {
   int* slot;
   int ring, cap, window, q_pos0, n_q;
 };
+
+// Kernel arguments travel by value; keep each struct within 4 KiB.
+static_assert(sizeof(PrefillPrepArgs) <= 4096, "kernel argument size");
+static_assert(sizeof(RingCopyArgs) <= 4096, "kernel argument size");
+static_assert(sizeof(PrefillAttnArgs) <= 4096, "kernel argument size");
+static_assert(sizeof(DecodeArgs) <= 4096, "kernel argument size");
+static_assert(sizeof(RopeApplyArgs) <= 4096, "kernel argument size");
 
 hipError_t launch_prefill_prep(const PrefillPrepArgs& a, hipStream_t s);
 hipError_t launch_ring_to_stage(const RingCopyArgs& a, hipStream_t s);

@@ -147,18 +147,22 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   __shared__ __attribute__((aligned(1024))) char v_lds0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char v_lds1[kTileBytes];
 
-  // Longest query blocks first; then sequence, then KV head.
+  // Longest query blocks first; then sequence, then KV head. In a ragged
+  // batch the blocks past a shorter sequence's end leave at once.
   const int per_qt = a.B * a.Hkv;
   const int qt = a.q_tiles - 1 - (int)blockIdx.x / per_qt;
   const int r2 = (int)blockIdx.x % per_qt;
   const int b = r2 / a.Hkv;
   const int kvh = r2 % a.Hkv;
+  const int len = a.len[b];
+  if (qt * kBM >= len) return;
+  const size_t tok0 = (size_t)a.tok0[b];  // packed row of the sequence's query 0
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = kvh * kGroup + wave;
   const int q0 = qt * kBM;
-  const int nq = min(kBM, a.S - q0);
+  const int nq = min(kBM, len - q0);
   const int pq_first = a.start[b] + q0;
   const int pq_last = pq_first + nq - 1;
   const int kp0 = a.key_pos0[b];
@@ -211,16 +215,16 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   // (B operand of S^T): lane holds query lane % 32, channels
   // ks*16 + (lane / 32)*8 .. +7 for ks = 0..15.
   const int qrow = q0 + (lane & 31);
-  const bool qvalid = qrow < a.S;
+  const bool qvalid = qrow < len;
   // the gate logit, requested now and used in the epilogue
-  const size_t orow = ((size_t)b * a.S + (qvalid ? qrow : a.S - 1)) * a.Hq + h;
+  const size_t orow = (tok0 + (qvalid ? qrow : len - 1)) * a.Hq + h;
   const uint16_t gate_bits = a.gate[orow];
   bf16x8 qf[16];
   {
-    const int qr = qvalid ? qrow : a.S - 1;
-    const uint16_t* qp = a.q + (((size_t)b * a.S + qr) * a.Hq + h) * kHeadDim;
+    const int qr = qvalid ? qrow : len - 1;
+    const uint16_t* qp = a.q + ((tok0 + qr) * a.Hq + h) * kHeadDim;
     const int half = a.r >> 1;
-    const float2* tp = a.table + ((size_t)b * a.S + qr) * half;
+    const float2* tp = a.table + (tok0 + qr) * half;
     // With r a multiple of 32 (the pages' 64 and 256), the partner of
     // fragment ks (channels 16ks + 8(lane/32) ..) is fragment ks +- r/32 of
     // the same lane: every load is issued up front, in one round trip, and
@@ -531,8 +535,8 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
     for (int k = 0; k < 16; ++k) {
       const int r = 2 * k + (lane >> 5);
       const uint4 v = *(const uint4*)(stage + r * 512 + (((lane & 31) ^ r) << 4));
-      if (q0 + r < a.S)
-        *(uint4*)(a.out + (((size_t)b * a.S + q0 + r) * a.Hq + h) * kHeadDim + (lane & 31) * 8) = v;
+      if (q0 + r < len)
+        *(uint4*)(a.out + ((tok0 + q0 + r) * a.Hq + h) * kHeadDim + (lane & 31) * 8) = v;
     }
   }
 }

@@ -24,13 +24,17 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(PrefillPrepA
   __shared__ double sn[kPrepTokens][128];
   const int i0 = blockIdx.x * kPrepTokens;
   const int b = blockIdx.y;
+  const int len = a.len[b];
+  if (i0 >= len) return;  // a shorter sequence of a ragged batch
   const int t = threadIdx.x;
   const int half = a.r >> 1;
-  const int ntok = min(kPrepTokens, a.S - i0);
+  const int ntok = min(kPrepTokens, len - i0);
   const int nchunk = ntok * a.Hkv * 32;
+  const size_t row0 = (size_t)a.tok0[b] + i0;  // packed row of the block's first token
+  const int ring_from = len - min(len, a.ring_cap);
 
   // chunk c: token c / (32 Hkv), head (c / 32) % Hkv, channels 8(c % 32) .. +7
-  auto src_off = [&](int c) { return (((size_t)b * a.S + i0 + c / (a.Hkv * 32)) * a.Hkv + (c >> 5) % a.Hkv) * kHeadDim; };
+  auto src_off = [&](int c) { return ((row0 + c / (a.Hkv * 32)) * a.Hkv + (c >> 5) % a.Hkv) * kHeadDim; };
   auto partner = [&](int ch) {  // chunk holding the RoPE partners of chunk ch
     const int d0 = ch * 8;
     return d0 < a.r ? (d0 < half ? d0 + half : d0 - half) >> 3 : ch;
@@ -56,7 +60,7 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(PrefillPrepA
     const size_t o = (((size_t)b * a.Hkv + h) * a.dst_rows + a.dst_row0[b] + i) * kHeadDim;
     ((uint4*)(a.dst_k + o))[ch] = ko;
     ((uint4*)(a.dst_v + o))[ch] = vx;
-    if (a.ring_k && i >= a.ring_from) {
+    if (a.ring_k && i >= ring_from) {
       const int slot = (a.start[b] + i) % a.ring_cap;
       const size_t ro = (((size_t)b * a.Hkv + h) * a.ring_cap + slot) * kHeadDim;
       ((uint4*)(a.ring_k + ro))[ch] = ko;
@@ -82,7 +86,7 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(PrefillPrepA
     rope_sincos(a.start[b] + i0 + tok, a.inv_freq[j], &s, &c);
     cs[tok][j] = c;
     sn[tok][j] = s;
-    a.table[((size_t)b * a.S + i0 + tok) * half + j] = make_float2((float)c, (float)s);
+    a.table[(row0 + tok) * half + j] = make_float2((float)c, (float)s);
   }
   __syncthreads();
 #pragma unroll
@@ -155,8 +159,8 @@ __global__ __launch_bounds__(256) void index_probe_kernel(ProbeArgs a) {
 }
 
 hipError_t launch_prefill_prep(const PrefillPrepArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(prefill_prep_kernel, dim3((a.S + kPrepTokens - 1) / kPrepTokens, a.B), dim3(kPrepThreads), 0, s,
-                     a);
+  hipLaunchKernelGGL(prefill_prep_kernel, dim3((a.max_len + kPrepTokens - 1) / kPrepTokens, a.B),
+                     dim3(kPrepThreads), 0, s, a);
   return hipGetLastError();
 }
 

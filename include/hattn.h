@@ -139,6 +139,32 @@ int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k,
                   const hattn_kv_cache* cache, void* out, void* workspace,
                   size_t workspace_bytes, hipStream_t stream);
 
+/* Ragged prefill: sequences with different numbers of new tokens in one
+ * call (same page passages as hattn_prefill). New tokens are packed:
+ *   cu_seqlens: int32 [B+1], HOST memory, cu_seqlens[0] = 0 and
+ *     non-decreasing; sequence b's new tokens are packed rows
+ *     cu_seqlens[b] .. cu_seqlens[b+1]-1 (none when equal).
+ *   q: bf16 [T][num_q_heads][256], k, v: bf16 [T][num_kv_heads][256],
+ *   gate: bf16 [T][num_q_heads], out: bf16 [T][num_q_heads][256], with
+ *   T = cu_seqlens[B].
+ *   start_pos, cache, workspace, stream: as for hattn_prefill; sequence b's
+ *   token i sits at position start_pos[b] + i.
+ * With every length equal to S this is hattn_prefill (the same layout, the
+ * same kernels, the same bits). A sequence with no new tokens leaves its
+ * cache untouched. Errors as for hattn_prefill; a decreasing or not
+ * zero-based cu_seqlens is HATTN_ERR_SHAPE. */
+size_t hattn_prefill_varlen_workspace_size(const hattn_layer_desc* desc,
+                                           const hattn_kv_cache* cache,
+                                           int32_t batch,
+                                           const int32_t* cu_seqlens);
+int hattn_prefill_varlen(const hattn_layer_desc* desc, const void* q,
+                         const void* k, const void* v, const void* gate,
+                         int32_t batch, const int32_t* cu_seqlens,
+                         const int32_t* start_pos,
+                         const hattn_kv_cache* cache, void* out,
+                         void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
 /* Bytes of device workspace hattn_decode needs for a batch. */
 size_t hattn_decode_workspace_size(const hattn_layer_desc* desc,
                                    const hattn_kv_cache* cache, int32_t batch);

@@ -289,6 +289,41 @@ def prefill_ref(q, k, v, gate, start_pos, *, window, theta, rotary_fraction,
     return out, k_hat_all
 
 
+def prefill_varlen_ref(q, k, v, gate, cu_seqlens, start_pos, *, window, theta,
+                       rotary_fraction, hist_k=None, hist_v=None, hist_pos=None,
+                       round_keys=True, gate_act="sigmoid"):
+    """A ragged batch of prefills: sequence b's new tokens are the packed
+    rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of q [T, Hq, D], k/v [T, Hkv, D]
+    and gate [T, Hq], at positions start_pos[b] + 0, 1, ...; each sequence
+    is its own prefill_ref call over its own history (hist_* indexed by b as
+    in prefill_ref). Returns (out [T, Hq, D], k_hat [T, Hkv, D]) in packed
+    order."""
+    q = f64(q)
+    k = f64(k)
+    v = f64(v)
+    gate = f64(gate)
+    cu = [int(x) for x in cu_seqlens]
+    T = q.shape[0]
+    if cu[0] != 0 or cu[-1] != T or any(b > a for a, b in zip(cu[1:], cu[:-1])):
+        raise ValueError("cu_seqlens must start at 0, not decrease and end at T")
+    out = np.zeros(q.shape)
+    k_hat = np.zeros(k.shape)
+    for b in range(len(cu) - 1):
+        lo, hi = cu[b], cu[b + 1]
+        if hi == lo:
+            continue
+        hist = {}
+        if hist_k is not None:
+            hist = dict(hist_k=hist_k[b:b + 1], hist_v=hist_v[b:b + 1], hist_pos=hist_pos[b:b + 1])
+        o, kh = prefill_ref(q[None, lo:hi], k[None, lo:hi], v[None, lo:hi], gate[None, lo:hi],
+                            [start_pos[b]], window=window, theta=theta,
+                            rotary_fraction=rotary_fraction, round_keys=round_keys,
+                            gate_act=gate_act, **hist)
+        out[lo:hi] = o[0]
+        k_hat[lo:hi] = kh[0]
+    return out, k_hat
+
+
 def decode_ref(q, k, v, gate, pos, cache_k, cache_v, *, kind, window, theta,
                rotary_fraction, round_keys=True, gate_act="sigmoid"):
     """One decode step: one new token per sequence at position pos[b].

@@ -103,6 +103,39 @@ def test_prefill_rejects_bad_arguments(L):
         assert got == want, (desc.layer_type, kw, got, want)
 
 
+def _varlen(L, desc, cache, cu, start, ws_bytes=1 << 30):
+    B = len(cu) - 1
+    cu_a = (ctypes.c_int32 * len(cu))(*cu)
+    sp = (ctypes.c_int32 * B)(*start)
+    return L.hattn_prefill_varlen(ctypes.byref(desc), FAKE, FAKE, FAKE, FAKE, B, ctypes.cast(cu_a, ctypes.c_void_p),
+                                  ctypes.cast(sp, ctypes.c_void_p), ctypes.byref(cache), FAKE, FAKE, ws_bytes,
+                                  None)
+
+
+def test_prefill_varlen_rejects_bad_arguments(L):
+    fu = hb.layer_desc("full")
+    lin = hb.KvCacheC(FAKE, FAKE, hb.KV_LINEAR, 3, 64)
+    assert _varlen(L, fu, lin, [1, 5, 9, 12], [0, 0, 0]) == -2          # not zero-based
+    assert _varlen(L, fu, lin, [0, 5, 4, 12], [0, 0, 0]) == -2          # decreasing
+    assert _varlen(L, fu, lin, [0, 5, 9, 12], [0, 61, 0]) == -7         # 61 + 4 > 64
+    assert _varlen(L, fu, lin, [0, 5, 9, 12], [0, -1, 0]) == -11
+    assert _varlen(L, fu, lin, [0, 5, 9, 12], [0, 0, 0], ws_bytes=16) == -8
+    assert _varlen(L, fu, hb.KvCacheC(FAKE, FAKE, hb.KV_LINEAR, 2, 64), [0, 5, 9, 12], [0, 0, 0]) == -6
+    assert _varlen(L, fu, lin, [0, 0, 0, 0], [0, 0, 0]) == 0            # nothing to do
+    sp = (ctypes.c_int32 * 3)(0, 0, 0)
+    assert L.hattn_prefill_varlen(ctypes.byref(fu), FAKE, FAKE, FAKE, FAKE, 3, None, ctypes.cast(sp, ctypes.c_void_p),
+                                  ctypes.byref(lin), FAKE, FAKE, 1 << 30, None) == -1
+    # workspace: the cos/sin table of the packed tokens (r/2 fp32 pairs each);
+    # a ring adds K/V staging of window - 1 + the longest sequence's rows
+    cu = (ctypes.c_int32 * 4)(0, 100, 130, 400)
+    assert L.hattn_prefill_varlen_workspace_size(ctypes.byref(fu), ctypes.byref(lin), 3,
+                                                 ctypes.cast(cu, ctypes.c_void_p)) == 400 * 32 * 8
+    sl = hb.layer_desc("sliding")
+    ring = hb.KvCacheC(FAKE, FAKE, hb.KV_RING, 3, 512)
+    got = L.hattn_prefill_varlen_workspace_size(ctypes.byref(sl), ctypes.byref(ring), 3, ctypes.cast(cu, ctypes.c_void_p))
+    assert got == 400 * 128 * 8 + 2 * 3 * 4 * (511 + 270) * 256 * 2
+
+
 def test_decode_rejects_bad_arguments(L):
     sl = hb.layer_desc("sliding")
     fu = hb.layer_desc("full")

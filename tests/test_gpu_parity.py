@@ -267,6 +267,57 @@ def test_prefill_and_decode_other_rotary_widths(fraction):
     check_decode_cache(cache, dinp, slots, k_hat_d)
 
 
+@pytest.mark.parametrize("layer,kind,cap", [("sliding", "ring", 512), ("full", "linear", 2048)])
+def test_varlen_prefill_ragged_batch(layer, kind, cap):
+    # eight sequences of 0 .. 600 new tokens over cached histories, in one call
+    lens = [0, 1, 77, 300, 31, 64, 129, 600]
+    starts = [5, 0, 1000, 3, 511, 700, 2, 40]
+    B, T = len(lens), sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    desc = hb.layer_desc(layer)
+    inp = {n: t[0] for n, t in synth.prefill_inputs(1, T, 16, 4, seed=90).items()}
+    ck = synth.cache_tensor(B, 4, cap, seed=91)
+    cv = synth.cache_tensor(B, 4, cap, seed=92)
+    cache = hb.KVCache(ck.to(DEV), cv.to(DEV), kind)
+    d = to_dev(inp)
+    out = hb.hattn_prefill_varlen(desc, d["q"], d["k"], d["v"], d["gate"], cu, starts, cache)
+    torch.cuda.synchronize()
+    hk, hv, hp = history_for(kind, ck, cv, starts, cap)
+    w = desc.window if desc.window > 0 else None
+    ref, k_hat = O.prefill_varlen_ref(inp["q"], inp["k"], inp["v"], inp["gate"], cu, starts, window=w,
+                                      theta=desc.rope_theta, rotary_fraction=desc.rotary_fraction,
+                                      hist_k=hk, hist_v=hv, hist_pos=hp)
+    check(f"varlen prefill {layer} lengths {lens}", out.cpu(), ref)
+    for b in range(B):
+        n = lens[b]
+        if n == 0:
+            assert torch.equal(cache.k[b].cpu(), ck[b]) and torch.equal(cache.v[b].cpu(), cv[b])
+            continue
+        keep = min(n, cap) if kind == "ring" else n
+        pos = np.arange(starts[b] + n - keep, starts[b] + n)
+        slots = pos % cap if kind == "ring" else pos
+        rows = cu[b] + pos - starts[b]
+        check_bf16_values(f"varlen cache keys b={b}", cache.k[b, :, slots].cpu().permute(1, 0, 2), k_hat[rows])
+        assert torch.equal(cache.v[b, :, slots].cpu().permute(1, 0, 2), inp["v"][rows])
+
+
+def test_varlen_prefill_with_equal_lengths_is_bitwise_the_batched_call():
+    B, S, starts = 3, 100, [0, 50, 700]
+    desc = hb.layer_desc("sliding")
+    inp = to_dev(synth.prefill_inputs(B, S, 16, 4, seed=93))
+    ck = synth.cache_tensor(B, 4, 512, seed=94).to(DEV)
+    cv = synth.cache_tensor(B, 4, 512, seed=95).to(DEV)
+    c1 = hb.KVCache(ck.clone(), cv.clone(), "ring")
+    c2 = hb.KVCache(ck.clone(), cv.clone(), "ring")
+    o1 = hb.hattn_prefill(desc, inp["q"], inp["k"], inp["v"], inp["gate"], starts, c1)
+    pk = lambda t: t.reshape((B * S,) + tuple(t.shape[2:]))
+    o2 = hb.hattn_prefill_varlen(desc, pk(inp["q"]), pk(inp["k"]), pk(inp["v"]), pk(inp["gate"]),
+                                 [0, S, 2 * S, 3 * S], starts, c2)
+    torch.cuda.synchronize()
+    assert torch.equal(pk(o1), o2)
+    assert torch.equal(c1.k, c2.k) and torch.equal(c1.v, c2.v)
+
+
 def test_prefill_window_one_and_peaky():
     desc, inp, ck, cv, cache, out = run_prefill("sliding", 1, 300, 16, 4, [0], 4, "linear", 300, window=1)
     ref, _ = oracle_prefill(desc, inp, ck, cv, [0], "linear", 300)

@@ -163,8 +163,8 @@ def test_ring_slots_by_brute_force_replay():
             assert all(O.ring_slot(p, cap) == p % cap for p in range(n))
 
 
-def _small_prefill(S=37, Hq=4, Hkv=2, seed=0, q_scale=1.0):
-    inp = synth.prefill_inputs(1, S, Hq, Hkv, seed=seed, q_scale=q_scale)
+def _small_prefill(S=37, Hq=4, Hkv=2, seed=0, q_scale=1.0, B=1):
+    inp = synth.prefill_inputs(B, S, Hq, Hkv, seed=seed, q_scale=q_scale)
     return {k: O.f64(v) for k, v in inp.items()}
 
 
@@ -278,6 +278,48 @@ def test_silu_gate_in_decode_equals_prefill_row():
     dec, _, _ = O.decode_ref(q[:, S - 1], k[:, S - 1], v[:, S - 1], g[:, S - 1], [S - 1], ck, cv,
                              kind="linear", **kw)
     np.testing.assert_allclose(dec[0], pre[0, S - 1], rtol=1e-12, atol=1e-14)
+
+
+def test_varlen_prefill_equal_lengths_is_the_uniform_batch():
+    x = _small_prefill(S=12, seed=21, B=3)
+    kw = dict(window=5, theta=1e4, rotary_fraction=1.0)
+    out, kh = O.prefill_ref(x["q"], x["k"], x["v"], x["gate"], [0, 7, 30], **kw)
+    pk = lambda t: O.f64(t).reshape((-1,) + tuple(t.shape[2:]))
+    vo, vk = O.prefill_varlen_ref(pk(x["q"]), pk(x["k"]), pk(x["v"]), pk(x["gate"]), [0, 12, 24, 36],
+                                  [0, 7, 30], **kw)
+    assert np.array_equal(vo, out.reshape(vo.shape)) and np.array_equal(vk, kh.reshape(vk.shape))
+
+
+def test_varlen_prefill_sequences_are_independent():
+    # ragged lengths (one empty): each sequence's rows equal a batch of one,
+    # whatever the others hold, and the empty one produces nothing
+    rng = np.random.default_rng(22)
+    lens, starts = [5, 0, 9, 1], [3, 11, 0, 40]
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q = rng.standard_normal((T, 8, 256))
+    k = O.bf16_rne(rng.standard_normal((T, 2, 256)))
+    v = O.bf16_rne(rng.standard_normal((T, 2, 256)))
+    g = 2.0 * rng.standard_normal((T, 8))
+    hk = O.bf16_rne(rng.standard_normal((4, 2, 64, 256)))
+    hv = O.bf16_rne(rng.standard_normal((4, 2, 64, 256)))
+    hp = np.stack([O.linear_slot_positions(s, 64) for s in starts])
+    kw = dict(window=None, theta=5e6, rotary_fraction=0.25)
+    out, kh = O.prefill_varlen_ref(q, k, v, g, cu, starts, hist_k=hk, hist_v=hv, hist_pos=hp, **kw)
+    for b in range(4):
+        lo, hi = cu[b], cu[b + 1]
+        if hi == lo:
+            continue
+        o1, k1 = O.prefill_ref(q[None, lo:hi], k[None, lo:hi], v[None, lo:hi], g[None, lo:hi], [starts[b]],
+                               hist_k=hk[b:b + 1], hist_v=hv[b:b + 1], hist_pos=hp[b:b + 1], **kw)
+        assert np.array_equal(out[lo:hi], o1[0]) and np.array_equal(kh[lo:hi], k1[0])
+    # changing another sequence's tokens leaves sequence 2 unchanged
+    q2 = q.copy()
+    q2[:cu[2]] += 1.0
+    out2, _ = O.prefill_varlen_ref(q2, k, v, g, cu, starts, hist_k=hk, hist_v=hv, hist_pos=hp, **kw)
+    assert np.array_equal(out2[cu[2]:cu[3]], out[cu[2]:cu[3]])
+    with pytest.raises(ValueError):
+        O.prefill_varlen_ref(q, k, v, g, [0, 5, 4, 15, 15], starts, **kw)
 
 
 def test_new_keys_are_cached_as_bf16():
