@@ -99,6 +99,22 @@ def copy_calibration():
             "launches": 3}
 
 
+def to_paged(torch, hb, ck, cv, page, seed):
+    """A paged copy of linear caches [B, Hkv, cap, 256]: the B * cap / page
+    pages in a seeded random order in one pool, and the block table that
+    maps them back."""
+    B, H, cap, D = ck.shape
+    n = cap // page
+    perm = torch.randperm(B * n, generator=torch.Generator().manual_seed(seed))
+
+    def pool(x):
+        p = torch.empty((B * n, H, page, D), dtype=x.dtype, device=x.device)
+        p[perm.to(x.device)] = x.view(B, H, n, page, D).permute(0, 2, 1, 3, 4).reshape(B * n, H, page, D)
+        return p
+
+    return hb.KVCache.paged(pool(ck), pool(cv), perm.view(B, n).to(torch.int32).to(ck.device))
+
+
 def time_calls(torch, fn, steps, warmup):
     for _ in range(warmup):
         fn()
@@ -214,12 +230,14 @@ def run(args):
     if not args.skip_prefill_configs:
         prefill_configs = {}
 
-        def prefill_case(layer, B, S_, Hq_, Hkv_, s0, cap, kind, fill, seed, steps, warmup):
+        def prefill_case(layer, B, S_, Hq_, Hkv_, s0, cap, kind, fill, seed, steps, warmup, page=None):
             d = hb.layer_desc(layer, Hq_, Hkv_)
             pin = {k: v.to(dev) for k, v in synth.prefill_inputs(B, S_, Hq_, Hkv_, seed=seed).items()}
             c = hb.KVCache(synth.cache_tensor(B, Hkv_, cap, seed=seed + 1, fill_tokens=fill, threads=16).to(dev),
                            synth.cache_tensor(B, Hkv_, cap, seed=seed + 2, fill_tokens=fill, threads=16).to(dev),
                            kind)
+            if page:
+                c = to_paged(torch, hb, c.k, c.v, page, seed + 3)
             o = torch.empty_like(pin["q"])
             w = torch.empty(max(hb.prefill_workspace_size(d, c, B, S_), 256), dtype=torch.uint8, device=dev)
             starts = [s0] * B
@@ -250,6 +268,16 @@ def run(args):
         tf28 = fl28 / (ms28 * 1e-3) / 1e12
         log(f"prefill 1.7B chunk (28 layers): {ms28:.2f} ms, {tf28:.1f} TFLOP/s "
             f"(sliding layer {ts['median']:.3f} ms, full layer {tfu['median']:.3f} ms)")
+        # the same full-layer call on a paged cache (pages of 256 slots in a
+        # shuffled pool)
+        tpg, _ = prefill_case("full", 2, S5, 8, 2, s0, s0 + S5, "linear", s0, 50, 5, 2, page=256)
+        torch.cuda.empty_cache()
+        log(f"prefill 1.7B full layer, paged cache (256-slot pages): {tpg['median']:.3f} ms "
+            f"({flf / (tpg['median'] * 1e-3) / 1e12:.1f} TFLOP/s)")
+        prefill_configs["chunked_1p7b_full_layer_paged256"] = {
+            "ms": {k: round(v, 4) for k, v in tpg.items()}, "flop": flf,
+            "TFLOP_per_s": round(flf / (tpg["median"] * 1e-3) / 1e12, 2),
+            "linear_cache_ms": round(tfu["median"], 4)}
         prefill_configs["chunked_1p7b_28_layers"] = {
             "ms_28_layers": round(ms28, 3), "flop_28_layers": fl28, "TFLOP_per_s": round(tf28, 2),
             "frac_bf16_peak": round(tf28 / PEAK_BF16_TFLOPS, 4),
@@ -272,7 +300,7 @@ def run(args):
             pos_d = torch.as_tensor(pos, dtype=torch.int32).to(dev)
             o = torch.empty_like(dinp["q"])
             maxp = int(max(pos))
-            cs = [hb.KVCache(ck, cv, kind) for ck, cv in caches]
+            cs = [c if isinstance(c, hb.KVCache) else hb.KVCache(c[0], c[1], kind) for c in caches]
             wsd = torch.empty(max(hb.decode_workspace_size(desc, cs[0], B), 256), dtype=torch.uint8, device=dev)
             it = [0]
 
@@ -312,7 +340,12 @@ def run(args):
         m = n // 8
         decode_case("full_b8_131072", full, 8, m, "linear", [m - 1] * 8,
                     [(ck.view(8, Hkv, m, 256), cv.view(8, Hkv, m, 256))])
+        # the 1M-token decode on a paged copy (4096 pages of 256 slots, shuffled)
+        pg = to_paged(torch, hb, ck, cv, 256, 7)
         del ck, cv
+        torch.cuda.empty_cache()
+        decode_case("full_b1_1M_paged256", full, 1, n, "paged", [n - 1], [pg])
+        del pg
         torch.cuda.empty_cache()
 
     line = {

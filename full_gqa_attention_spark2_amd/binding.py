@@ -18,7 +18,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "hattn.h")
 
 LAYER_SLIDING, LAYER_FULL = 0, 1
 GATE_SIGMOID, GATE_SILU = 0, 1
-KV_RING, KV_LINEAR = 0, 1
+KV_RING, KV_LINEAR, KV_PAGED = 0, 1, 2
 HEAD_DIM = 256
 
 
@@ -48,6 +48,9 @@ class KvCacheC(ctypes.Structure):
         ("kind", ctypes.c_int32),
         ("batch", ctypes.c_int32),
         ("capacity", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("block_table", ctypes.c_void_p),
+        ("num_pages", ctypes.c_int32),
     ]
 
 
@@ -161,23 +164,46 @@ def layer_desc(layer_type, num_q_heads=16, num_kv_heads=4, **overrides) -> Layer
 
 
 class KVCache:
-    """A layer's cache: K and V bf16 [B, Hkv, capacity, 256] on the GPU."""
+    """A layer's cache: K and V bf16 [B, Hkv, capacity, 256] on the GPU; or,
+    for a paged cache (KVCache.paged), page pools [num_pages, Hkv,
+    page_size, 256] with an int32 block table [B, capacity / page_size]."""
 
     def __init__(self, k, v, kind):
         self.k, self.v = k, v
         self.kind = {"ring": KV_RING, "linear": KV_LINEAR}.get(kind, kind)
+        self.block_table = None
         _need(k, "cache.k")
         _need(v, "cache.v", shape=k.shape)
         if k.dim() != 4 or k.shape[3] != HEAD_DIM:
             raise ValueError("cache tensors must be [B, Hkv, capacity, 256]")
+        self.batch, self.capacity = k.shape[0], k.shape[2]
 
     @classmethod
     def empty(cls, B, Hkv, capacity, kind, device="cuda"):
         k = torch.zeros((B, Hkv, capacity, HEAD_DIM), dtype=torch.bfloat16, device=device)
         return cls(k, torch.zeros_like(k), kind)
 
+    @classmethod
+    def paged(cls, k_pool, v_pool, block_table):
+        """Pools bf16 [num_pages, Hkv, page_size, 256] and a device int32
+        block table [B, pages_per_seq]: sequence b's slot p is row
+        p % page_size of page block_table[b, p // page_size]."""
+        c = cls.__new__(cls)
+        _need(k_pool, "cache.k")
+        _need(v_pool, "cache.v", shape=k_pool.shape)
+        _need(block_table, "block_table", torch.int32)
+        if k_pool.dim() != 4 or k_pool.shape[3] != HEAD_DIM or block_table.dim() != 2:
+            raise ValueError("pools must be [num_pages, Hkv, page_size, 256], the table [B, pages]")
+        c.k, c.v, c.kind, c.block_table = k_pool, v_pool, KV_PAGED, block_table
+        c.page_size = k_pool.shape[2]
+        c.batch, c.capacity = block_table.shape[0], block_table.shape[1] * c.page_size
+        return c
+
     def c(self) -> KvCacheC:
-        return KvCacheC(self.k.data_ptr(), self.v.data_ptr(), self.kind, self.k.shape[0], self.k.shape[2])
+        if self.kind == KV_PAGED:
+            return KvCacheC(self.k.data_ptr(), self.v.data_ptr(), self.kind, self.batch, self.capacity,
+                            self.page_size, self.block_table.data_ptr(), self.k.shape[0])
+        return KvCacheC(self.k.data_ptr(), self.v.data_ptr(), self.kind, self.batch, self.capacity)
 
 
 def prefill_workspace_size(desc, cache, B, S):

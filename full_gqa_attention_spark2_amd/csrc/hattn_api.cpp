@@ -13,6 +13,7 @@
 using namespace hattn;
 
 static_assert(sizeof(hattn_layer_desc) == 40, "hattn_layer_desc layout is part of the ABI");
+static_assert(sizeof(hattn_kv_cache) == 48, "hattn_kv_cache layout is part of the ABI");
 
 namespace {
 
@@ -65,10 +66,30 @@ int check_cache(const hattn_layer_desc* d, const hattn_kv_cache* c, int batch) {
   if (c->batch != batch || c->capacity < 1) return HATTN_ERR_CACHE;
   if (c->kind == HATTN_KV_RING) {
     if (d->layer_type != HATTN_LAYER_SLIDING || c->capacity != d->window) return HATTN_ERR_CACHE;
+  } else if (c->kind == HATTN_KV_PAGED) {
+    // full layers only; pages of whole 64-row tiles; one table row per sequence
+    if (d->layer_type != HATTN_LAYER_FULL) return HATTN_ERR_CACHE;
+    if (c->page_size < kMinPageSize || c->page_size % kMinPageSize || c->capacity % c->page_size)
+      return HATTN_ERR_CACHE;
+    if (c->capacity / c->page_size > kMaxPagesPerSeq || c->num_pages < 1) return HATTN_ERR_CACHE;
+    if (!c->block_table) return HATTN_ERR_NULL;
+    if ((uintptr_t)c->block_table & 3u) return HATTN_ERR_ALIGN;
   } else if (c->kind != HATTN_KV_LINEAR) {
     return HATTN_ERR_CACHE;
   }
   return HATTN_OK;
+}
+
+// The kernels' view of a paged cache (table == nullptr otherwise).
+PagedKv paged_view(const hattn_kv_cache* c) {
+  PagedKv p{};
+  if (c->kind == HATTN_KV_PAGED) {
+    p.table = c->block_table;
+    p.page_size = c->page_size;
+    p.pages_per_seq = c->capacity / c->page_size;
+    p.num_pages = c->num_pages;
+  }
+  return p;
 }
 
 hattn_status from_hip(hipError_t e) { return e == hipSuccess ? HATTN_OK : HATTN_ERR_LAUNCH; }
@@ -271,8 +292,9 @@ int prefill_packed(const hattn_layer_desc* desc, const void* q, const void* k, c
     return HATTN_ERR_ALIGN;
   // The attention kernel addresses a (sequence, KV head) slab of key rows
   // with 32-bit byte offsets (512 B per row).
+  // (A paged cache is addressed per page.)
   const long long key_rows = ring ? (long long)desc->window - 1 + max_len : (long long)cache->capacity;
-  if (key_rows > kMaxPrefillKeyRows) return HATTN_ERR_UNSUPPORTED;
+  if (cache->kind != HATTN_KV_PAGED && key_rows > kMaxPrefillKeyRows) return HATTN_ERR_UNSUPPORTED;
   const PrefillLayout L = prefill_layout(desc, cache, batch, total, max_len);
   if (!workspace || workspace_bytes < L.total) return HATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return HATTN_ERR_ALIGN;
@@ -319,6 +341,7 @@ int prefill_packed(const hattn_layer_desc* desc, const void* q, const void* k, c
   ra.max_len = max_len;
   ra.Hkv = Hkv;
   ra.dst_rows = ring ? L.stage_rows : cache->capacity;
+  ra.paged = paged_view(cache);
   ra.r = r;
   // a ring keeps each sequence's last min(len, capacity) new tokens; the
   // prep kernel writes them to their slots (the history they replace is
@@ -354,6 +377,7 @@ int prefill_packed(const hattn_layer_desc* desc, const void* q, const void* k, c
   aa.Hq = Hq;
   aa.Hkv = Hkv;
   aa.rows = ring ? L.stage_rows : cache->capacity;
+  aa.paged = paged_view(cache);
   aa.window = desc->layer_type == HATTN_LAYER_SLIDING ? w : 0;
   aa.r = r;
   aa.gate_act = desc->gate_act;
@@ -444,7 +468,7 @@ int hattn_decode(const hattn_layer_desc* desc, const void* q, const void* k, con
       ((uintptr_t)pos & 3u))
     return HATTN_ERR_ALIGN;
   if (max_pos < 0 || max_pos >= kMaxPos) return HATTN_ERR_POSITION;
-  if (cache->kind == HATTN_KV_LINEAR && max_pos >= cache->capacity) return HATTN_ERR_CAPACITY;
+  if (cache->kind != HATTN_KV_RING && max_pos >= cache->capacity) return HATTN_ERR_CAPACITY;
   const long long span = decode_span(desc, cache, max_pos);
   const DecodePlan p = decode_plan(desc, cache, batch, span);
   const size_t parts = (size_t)batch * desc->num_q_heads * p.nsplit;
@@ -469,6 +493,7 @@ int hattn_decode(const hattn_layer_desc* desc, const void* q, const void* k, con
   a.Hkv = desc->num_kv_heads;
   a.cap = cache->capacity;
   a.ring = cache->kind == HATTN_KV_RING;
+  a.paged = paged_view(cache);
   a.window = desc->layer_type == HATTN_LAYER_SLIDING ? desc->window : 0;
   a.max_pos = max_pos;
   a.r = rotary_channels(desc->rotary_fraction, desc->head_dim);

@@ -76,6 +76,11 @@ __device__ __forceinline__ float group4_max(float x) {
 // with s(r) = r for K and 2r mod 16 for V: each DMA instruction fills one
 // 1 KiB block (rows 2u, 2u+1) and the XOR keeps the MFMA operand reads free
 // of bank conflicts.
+// kPaged: the cache is paged (a full layer, visible keys 0 .. p); the page
+// indices of the split's keys are staged in LDS once the position is known,
+// and each chunk (16 keys, inside one page) is read through a buffer
+// resource over its page.
+template <bool kPaged>
 __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char ring0[kWaves][2 * kChunkBytes];   // 64 KiB
   __shared__ __attribute__((aligned(1024))) char ring1[kWaves][2 * kChunkBytes];   // 64 KiB
@@ -89,6 +94,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t q_stage[kGroup][kHeadDim];  // 2 KiB
   __shared__ __attribute__((aligned(1024))) uint16_t kv_stage[2][512];           // 2 KiB
   __shared__ __attribute__((aligned(1024))) double freq_stage[128];              // 1 KiB
+  __shared__ int page_of[kPaged ? kMaxPagesPerSeq : 1];  // table entries of the split's pages
 
   const int sp = (int)blockIdx.x % a.nsplit;
   const int r2 = (int)blockIdx.x / a.nsplit;
@@ -132,30 +138,43 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
           __builtin_amdgcn_readfirstlane(lds_off(freq_stage)));
   }
 
-  const size_t kv_off = ((size_t)b * a.Hkv + kvh) * (size_t)a.cap * kHeadDim;
+  const size_t kv_off = kPaged ? 0 : ((size_t)b * a.Hkv + kvh) * (size_t)a.cap * kHeadDim;
   const uint32_t slab_bytes = (uint32_t)min((uint64_t)a.cap * 512u, (uint64_t)0xffffffffu);
   const i32x4 krs = slab_desc(a.kc + kv_off, slab_bytes);
   const i32x4 vrs = slab_desc(a.vc + kv_off, slab_bytes);
+  const int ps = kPaged ? a.paged.page_size : 1;
+  int pg_lo = 0;  // logical page of page_of[0]
 
   // DMA of the 16 keys from key0 into a slot: instruction u moves rows 2u,
   // 2u+1 (lane l: row 2u + l/32, piece (l%32) ^ s(row)). Row indices are
-  // clamped to last.
+  // clamped to last. With a paged cache the 16 rows lie in one page (key0 is
+  // a multiple of 16, the page size of 64) and last is in it too.
   auto load_rows = [&](int key0, int last, char* dst) __attribute__((always_inline)) {
     const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_off(dst));
+    i32x4 kr = krs, vr = vrs;
+    int base_row = 0;
+    if constexpr (kPaged) {
+      const int lp = key0 / ps;
+      const int pg = min(max(__builtin_amdgcn_readfirstlane(page_of[lp - pg_lo]), 0), a.paged.num_pages - 1);
+      const size_t off = ((size_t)pg * a.Hkv + kvh) * (size_t)ps * kHeadDim;
+      kr = slab_desc(a.kc + off, (uint32_t)ps * 512u);
+      vr = slab_desc(a.vc + off, (uint32_t)ps * 512u);
+      base_row = lp * ps;
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int row = 2 * u + (lane >> 5);
-      const uint32_t rowoff = (uint32_t)min(key0 + row, last) * 512u;
-      dma16(krs, rowoff + 16u * ((lane & 31) ^ row), l0 + u * 1024);
-      dma16(vrs, rowoff + 16u * ((lane & 31) ^ ((2 * row) & 15)), l0 + kChunkBytes + u * 1024);
+      const uint32_t rowoff = (uint32_t)(min(key0 + row, last) - base_row) * 512u;
+      dma16(kr, rowoff + 16u * ((lane & 31) ^ row), l0 + u * 1024);
+      dma16(vr, rowoff + 16u * ((lane & 31) ^ ((2 * row) & 15)), l0 + kChunkBytes + u * 1024);
     }
   };
 
   // Where the start of the visible range does not depend on the position
   // (ring caches, unbounded windows), the first chunk is requested now,
   // before the position has arrived; rows past the end of the visible range
-  // are fixed below.
-  const bool spec = (a.ring != 0 || a.window <= 0) && sp * a.split_keys + wave * kChunk < a.cap;
+  // are fixed below. (Not for a paged cache: its pages are staged first.)
+  const bool spec = !kPaged && (a.ring != 0 || a.window <= 0) && sp * a.split_keys + wave * kChunk < a.cap;
   const int spec_key0 = sp * a.split_keys + wave * kChunk;
   if (spec) {
     load_rows(spec_key0, a.cap - 1, ring0[wave]);
@@ -179,6 +198,15 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   const int k1 = min(k0 + a.split_keys, hi);
   const int slot = cache_slot(p, a.ring, a.cap);
   const int nchunks = k1 > k0 ? (k1 - k0 + kChunk - 1) / kChunk : 0;
+  if constexpr (kPaged) {
+    // the table entries of the pages holding keys k0 .. k1 - 1 (at most
+    // one table row); the caller's staging loads have all landed above
+    pg_lo = k0 / ps;
+    const int n_pg = k1 > k0 ? (k1 - 1) / ps - pg_lo + 1 : 0;
+    const int* tb = a.paged.table + (size_t)b * a.paged.pages_per_seq + pg_lo;
+    for (int i = t; i < n_pg; i += 256) page_of[i] = tb[i];
+    __syncthreads();
+  }
 
   // DMA of chunk c of this split into a slot; rows past the split end re-read
   // its last key (their scores are masked).
@@ -221,8 +249,17 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       if (d < a.r) y = d < half ? kx * c - kxp * s : kx * c + kxp * s;
       const uint16_t kh = double_to_bf16_bits(y);
       const uint16_t vn = kv_stage[1][d];
-      a.kc[kv_off + (size_t)slot * kHeadDim + d] = kh;
-      a.vc[kv_off + (size_t)slot * kHeadDim + d] = vn;
+      if constexpr (kPaged) {
+        const int pg = page_of[slot / ps - pg_lo];
+        if ((unsigned)pg < (unsigned)a.paged.num_pages) {  // else the write is dropped
+          const size_t o = (((size_t)pg * a.Hkv + kvh) * ps + slot % ps) * kHeadDim + d;
+          a.kc[o] = kh;
+          a.vc[o] = vn;
+        }
+      } else {
+        a.kc[kv_off + (size_t)slot * kHeadDim + d] = kh;
+        a.vc[kv_off + (size_t)slot * kHeadDim + d] = vn;
+      }
       newrow[0][d] = kh;
       newrow[1][d] = vn;
     }
@@ -486,7 +523,10 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const int grid = a.B * a.Hkv * a.nsplit;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_kernel, dim3(grid), dim3(256), 0, s, a);
+  if (a.paged.table)
+    hipLaunchKernelGGL(decode_kernel<true>, dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(decode_kernel<false>, dim3(grid), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(a.B * a.Hq), dim3(kMergeThreads), 0, s, a);

@@ -11,6 +11,18 @@ namespace hattn {
 constexpr int kMaxPrefillBatch = 128;
 constexpr int kPrefillBlockQ = 32;   // query positions per prefill workgroup
 constexpr long long kMaxPrefillKeyRows = 1LL << 23;  // key rows per (sequence, KV head) slab
+constexpr int kMaxPagesPerSeq = 4096;  // block-table entries per sequence of a paged cache
+constexpr int kMinPageSize = 64;       // a paged cache's page size is a multiple of this
+
+// A paged cache as the kernels see it: pool [num_pages][Hkv][page_size][256],
+// slot p of sequence b in page table[b * pages_per_seq + p / page_size].
+// table == nullptr: not paged.
+struct PagedKv {
+  const int* table;
+  int page_size;
+  int pages_per_seq;
+  int num_pages;
+};
 
 // Per new prefill token: cos/sin of its RoPE angles (fp32 table for the
 // attention kernel's query rotation) and its rotated key and value, written
@@ -24,7 +36,8 @@ struct PrefillPrepArgs {
   uint16_t* dst_k;
   uint16_t* dst_v;
   int B, max_len, Hkv;
-  int dst_rows;     // rows per (b, kv head) in dst
+  int dst_rows;     // rows per (b, kv head) in dst (not paged)
+  PagedKv paged;    // dst is a paged cache's pool (slot = position)
   int r;            // rotated channels
   uint16_t* ring_k; // ring cache that also receives each sequence's last
   uint16_t* ring_v; //   min(len, ring_cap) tokens (or null)
@@ -52,8 +65,9 @@ struct RingCopyArgs {
 struct PrefillAttnArgs {
   const uint16_t* q;      // bf16 [T][Hq][256], before RoPE
   const float2* table;    // [T][r/2] cos/sin of the query positions
-  const uint16_t* kc;     // bf16 [B][Hkv][rows][256], rotated keys
+  const uint16_t* kc;     // bf16 [B][Hkv][rows][256], rotated keys (or a paged pool)
   const uint16_t* vc;
+  PagedKv paged;          // key row j of sequence b is slot j of the paged cache
   const uint16_t* gate;   // bf16 [T][Hq]
   uint16_t* out;          // bf16 [T][Hq][256]
   int B, Hq, Hkv;
@@ -75,8 +89,9 @@ struct DecodeArgs {
   const uint16_t* v;
   const uint16_t* gate;   // bf16 [B][Hq]
   const int* pos;         // int32 [B], device
-  uint16_t* kc;           // cache [B][Hkv][cap][256]
+  uint16_t* kc;           // cache [B][Hkv][cap][256] (or a paged pool)
   uint16_t* vc;
+  PagedKv paged;
   uint16_t* out;          // bf16 [B][Hq][256]
   float* part_o;          // [B][Hq][nsplit][256]
   float* part_ml;         // [B][Hq][nsplit][2]

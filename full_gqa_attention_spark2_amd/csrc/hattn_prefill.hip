@@ -136,6 +136,11 @@ __device__ __forceinline__ void issue_order() {
 
 }  // namespace
 
+// kPaged: key row j of sequence b is slot j of a paged cache (a full layer's
+// positions 0 .. n_keys-1); its page indices for the workgroup's tiles are
+// staged in LDS first, and every tile (64 rows, inside one page) is read
+// through a buffer resource over its page.
+template <bool kPaged>
 __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a) {
   // Two K and two V tile slots (the swizzled block layout is described at
   // load_tile below). Four separate arrays (not one indexed array) so the
@@ -146,6 +151,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   __shared__ __attribute__((aligned(1024))) char k_lds1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char v_lds0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char v_lds1[kTileBytes];
+  __shared__ int page_of[kPaged ? kMaxPagesPerSeq : 1];  // pool page of logical page pg_lo + i
 
   // Longest query blocks first; then sequence, then KV head. In a ragged
   // batch the blocks past a shorter sequence's end leave at once.
@@ -173,11 +179,21 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   const int t_lo = row_lo / kBN;
   const int nt = (row_hi + kBN - 1) / kBN - t_lo;
 
-  const size_t kv_off = ((size_t)b * a.Hkv + kvh) * (size_t)a.rows * kHeadDim;
+  const size_t kv_off = kPaged ? 0 : ((size_t)b * a.Hkv + kvh) * (size_t)a.rows * kHeadDim;
   // the host limits a slab to 2^23 rows of 512 B
   const uint32_t slab_bytes = (uint32_t)min((uint64_t)a.rows * 512u, (uint64_t)0xffffffffu);
   const __amdgpu_buffer_rsrc_t krs = slab_rsrc(a.kc + kv_off, slab_bytes);
   const __amdgpu_buffer_rsrc_t vrs = slab_rsrc(a.vc + kv_off, slab_bytes);
+  const int ps = kPaged ? a.paged.page_size : 1;
+  const int pg_lo = kPaged ? t_lo * kBN / ps : 0;
+  if constexpr (kPaged) {
+    // the pages holding tiles t_lo .. t_lo + nt - 1 (at most the sequence's
+    // table row); entries outside the pool are clamped into it
+    const int n_pg = ((t_lo + nt) * kBN - 1) / ps - pg_lo + 1;
+    const int* tb = a.paged.table + (size_t)b * a.paged.pages_per_seq + pg_lo;
+    for (int i = threadIdx.x; i < n_pg; i += 256) page_of[i] = min(max(tb[i], 0), a.paged.num_pages - 1);
+    __syncthreads();
+  }
 
   // A K or V tile (64 key rows x 512 B) sits in LDS as 32 blocks of 1 KiB;
   // block 4g + c holds rows 8g .. 8g+7, bytes 128c .. 128c+127 of each row.
@@ -195,13 +211,23 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
       __attribute__((always_inline)) {
     char* dst = slot + wave * 8 * 1024;
     const int row0 = t * kBN + 16 * wave + (lane >> 3);
-    const uint32_t off0 = (uint32_t)min(row0, nk - 1) * 512u + chunk0;
-    const uint32_t off1 = (uint32_t)min(row0 + 8, nk - 1) * 512u + chunk1;
+    const int base_row = kPaged ? t * kBN / ps * ps : 0;  // first row of the tile's page
+    const uint32_t off0 = (uint32_t)(min(row0, nk - 1) - base_row) * 512u + chunk0;
+    const uint32_t off1 = (uint32_t)(min(row0 + 8, nk - 1) - base_row) * 512u + chunk1;
 #pragma unroll
     for (int u = 0; u < 8; ++u) load_lds16(rs, u < 4 ? off0 : off1, 128 * (u & 3), dst + u * 1024);
   };
-  auto load_k = [&](int t, char* slot) __attribute__((always_inline)) { load_tile(krs, k_chunk0, k_chunk1, t, slot); };
-  auto load_v = [&](int t, char* slot) __attribute__((always_inline)) { load_tile(vrs, v_chunk, v_chunk, t, slot); };
+  // Buffer resource over the page that holds tile t (paged caches).
+  auto page_rsrc = [&](const uint16_t* pool, int t) __attribute__((always_inline)) {
+    const int pg = __builtin_amdgcn_readfirstlane(page_of[t * kBN / ps - pg_lo]);
+    return slab_rsrc(pool + ((size_t)pg * a.Hkv + kvh) * (size_t)ps * kHeadDim, (uint32_t)ps * 512u);
+  };
+  auto load_k = [&](int t, char* slot) __attribute__((always_inline)) {
+    load_tile(kPaged ? page_rsrc(a.kc, t) : krs, k_chunk0, k_chunk1, t, slot);
+  };
+  auto load_v = [&](int t, char* slot) __attribute__((always_inline)) {
+    load_tile(kPaged ? page_rsrc(a.vc, t) : vrs, v_chunk, v_chunk, t, slot);
+  };
 
   // The first tiles: requested right after the query loads below, so they
   // are in flight during the query RoPE.
@@ -544,7 +570,10 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s) {
   const int grid = a.q_tiles * a.B * a.Hkv;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(prefill_attn_kernel, dim3(grid), dim3(256), 0, s, a);
+  if (a.paged.table)
+    hipLaunchKernelGGL(prefill_attn_kernel<true>, dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(prefill_attn_kernel<false>, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

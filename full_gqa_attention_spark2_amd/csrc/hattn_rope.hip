@@ -57,9 +57,20 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(PrefillPrepA
       }
     }
     const int i = i0 + tok;
-    const size_t o = (((size_t)b * a.Hkv + h) * a.dst_rows + a.dst_row0[b] + i) * kHeadDim;
-    ((uint4*)(a.dst_k + o))[ch] = ko;
-    ((uint4*)(a.dst_v + o))[ch] = vx;
+    if (a.paged.table) {  // slot = position, in the page the table names
+      const int p = a.start[b] + i;
+      const int ps = a.paged.page_size;
+      const int pg = a.paged.table[(size_t)b * a.paged.pages_per_seq + p / ps];
+      if ((unsigned)pg < (unsigned)a.paged.num_pages) {  // else the write is dropped
+        const size_t o = (((size_t)pg * a.Hkv + h) * ps + p % ps) * kHeadDim;
+        ((uint4*)(a.dst_k + o))[ch] = ko;
+        ((uint4*)(a.dst_v + o))[ch] = vx;
+      }
+    } else {
+      const size_t o = (((size_t)b * a.Hkv + h) * a.dst_rows + a.dst_row0[b] + i) * kHeadDim;
+      ((uint4*)(a.dst_k + o))[ch] = ko;
+      ((uint4*)(a.dst_v + o))[ch] = vx;
+    }
     if (a.ring_k && i >= ring_from) {
       const int slot = (a.start[b] + i) % a.ring_cap;
       const size_t ro = (((size_t)b * a.Hkv + h) * a.ring_cap + slot) * kHeadDim;

@@ -41,7 +41,9 @@
  *   - Caches store the rotated key and the value as bf16, layout
  *     [batch][num_kv_heads][capacity][head_dim]. A linear cache keeps
  *     position p in slot p. A ring cache (sliding layers only) has
- *     capacity == window and keeps position p in slot p mod capacity.
+ *     capacity == window and keeps position p in slot p mod capacity. A
+ *     paged cache (full layers only) keeps slot p in a page of a shared
+ *     pool (hattn_kv_cache below).
  *   - Positions are int32 in [0, 2^30).
  *   - Calls that touch the same cache must be ordered on one stream.
  */
@@ -64,7 +66,7 @@ typedef enum {
   HATTN_ERR_UNSUPPORTED = -3, /* head_dim != 256, group != 4, unknown gate_act  */
   HATTN_ERR_ROPE = -4,        /* theta <= 0 or head_dim*fraction not even int   */
   HATTN_ERR_WINDOW = -5,      /* sliding layer with window < 1, full with > 0   */
-  HATTN_ERR_CACHE = -6,       /* cache kind/capacity/batch does not fit layer   */
+  HATTN_ERR_CACHE = -6,       /* cache kind/capacity/batch/paging does not fit  */
   HATTN_ERR_CAPACITY = -7,    /* a position does not fit the linear cache       */
   HATTN_ERR_WORKSPACE = -8,   /* workspace NULL or smaller than required        */
   HATTN_ERR_ALIGN = -9,       /* a tensor pointer is not 16-byte aligned        */
@@ -77,7 +79,7 @@ typedef enum { HATTN_LAYER_SLIDING = 0, HATTN_LAYER_FULL = 1 } hattn_layer_type;
  * as in Eq. 1 and both released checkpoints, or silu(g) = g * sigmoid(g),
  * the alternative gate mode the model code supports. Evaluated in fp32. */
 typedef enum { HATTN_GATE_SIGMOID = 0, HATTN_GATE_SILU = 1 } hattn_gate_act;
-typedef enum { HATTN_KV_RING = 0, HATTN_KV_LINEAR = 1 } hattn_kv_kind;
+typedef enum { HATTN_KV_RING = 0, HATTN_KV_LINEAR = 1, HATTN_KV_PAGED = 2 } hattn_kv_kind;
 
 /* Parameters of one attention layer (page §1 config table, §2, §4 table). */
 typedef struct {
@@ -91,13 +93,32 @@ typedef struct {
   int32_t gate_act;        /* hattn_gate_act; 0 (sigmoid) unless set            */
 } hattn_layer_desc;
 
-/* A caller-owned KV cache of one layer. */
+/* A caller-owned KV cache of one layer.
+ *
+ * Ring and linear caches: k, v are bf16 [batch][num_kv_heads][capacity][256].
+ *
+ * Paged caches (full layers only; the serving setting of page §6's closing
+ * notes, where a 1M-token context's full-layer KV alone takes ~37 GB): k, v
+ * are a pool of pages, bf16 [num_pages][num_kv_heads][page_size][256], and
+ * block_table (DEVICE int32 [batch][capacity / page_size]) maps sequence
+ * b's slot p (the token at position p, as in a linear cache) to row
+ * p % page_size of page block_table[b][p / page_size]. page_size is a
+ * multiple of 64 and capacity a multiple of page_size with at most 4096
+ * pages per sequence. A table entry must name a pool page (0 .. num_pages-1)
+ * for every page that holds a position a call reads or writes; the kernels
+ * never touch memory outside the pool: an entry outside that range is
+ * clamped into it for reads (the result is then unspecified) and its writes
+ * are dropped. Pages may be shared between sequences only for positions
+ * no call writes. */
 typedef struct {
-  void* k;           /* bf16 [batch][num_kv_heads][capacity][head_dim]          */
+  void* k;           /* bf16 cache or page pool (layouts above)                 */
   void* v;           /* bf16, same layout                                       */
   int32_t kind;      /* hattn_kv_kind                                           */
   int32_t batch;     /* number of sequences                                     */
   int32_t capacity;  /* slots per (sequence, kv head); ring: == window          */
+  int32_t page_size; /* paged: slots per page; otherwise ignored                */
+  const int32_t* block_table; /* paged: device int32 [batch][capacity/page_size] */
+  int32_t num_pages; /* paged: pages in the pool                                */
 } hattn_kv_cache;
 
 /* Fill *out with the page's parameters of a layer type (§2, §4 table) for

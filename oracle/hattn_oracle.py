@@ -381,6 +381,22 @@ def decode_ref(q, k, v, gate, pos, cache_k, cache_v, *, kind, window, theta,
     return out, slots, k_hats
 
 
+def paged_to_linear(pool, table, page_size):
+    """The linear view [B, Hkv, pages_per_seq * page_size, D] of a paged
+    cache: pool [num_pages, Hkv, page_size, D], table [B, pages_per_seq];
+    slot p of sequence b is row p % page_size of page table[b, p //
+    page_size] (the layout the library documents for a paged cache, which
+    the pages leave to the implementation)."""
+    pool = np.asarray(pool)
+    table = np.asarray(table)
+    B, n = table.shape
+    out = np.zeros((B, pool.shape[1], n * page_size) + pool.shape[3:], dtype=pool.dtype)
+    for b in range(B):
+        for i in range(n):
+            out[b, :, i * page_size:(i + 1) * page_size] = pool[table[b, i]]
+    return out
+
+
 # --------------------------------------------------------------------------
 # KV-cache sizing  [SPARK §6 KV table]
 # --------------------------------------------------------------------------

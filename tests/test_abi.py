@@ -112,6 +112,28 @@ def _varlen(L, desc, cache, cu, start, ws_bytes=1 << 30):
                                   None)
 
 
+def test_paged_cache_validation(L):
+    assert ctypes.sizeof(hb.KvCacheC) == 48
+    fu = hb.layer_desc("full")
+    sl = hb.layer_desc("sliding")
+    def paged(cap=4096, ps=256, table=FAKE, pages=64, B=1):
+        return hb.KvCacheC(FAKE, FAKE, hb.KV_PAGED, B, cap, ps, table, pages)
+    # prefill: sliding layers take no paged cache; page size a multiple of 64
+    # dividing the capacity; at most 4096 pages per sequence; a table
+    assert _prefill(L, sl, paged()) == -6
+    assert _prefill(L, fu, paged(ps=96, cap=96 * 40)) == -6
+    assert _prefill(L, fu, paged(ps=256, cap=4096 + 64)) == -6
+    assert _prefill(L, fu, paged(ps=64, cap=64 * 4097)) == -6
+    assert _prefill(L, fu, paged(pages=0)) == -6
+    assert _prefill(L, fu, paged(table=0)) == -1
+    assert _prefill(L, fu, paged(table=FAKE + 2)) == -9
+    assert _prefill(L, fu, paged(), start=(4090,)) == -7          # 4090 + 8 > 4096
+    assert _decode(L, fu, paged(), max_pos=4096) == -7
+    assert _decode(L, fu, paged(ps=32, cap=320)) == -6
+    # workspace: the cos/sin table only (no staging)
+    assert L.hattn_prefill_workspace_size(ctypes.byref(fu), ctypes.byref(paged()), 1, 100) == 100 * 32 * 8
+
+
 def test_prefill_varlen_rejects_bad_arguments(L):
     fu = hb.layer_desc("full")
     lin = hb.KvCacheC(FAKE, FAKE, hb.KV_LINEAR, 3, 64)

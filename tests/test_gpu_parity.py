@@ -483,6 +483,84 @@ def test_planned_arena_layer_stack():
             assert torch.equal(arena[e.k_offset:e.k_offset + e.bytes // 2], before)
 
 
+def _paged_from_linear(lin_k, lin_v, page_size, extra_pages, seed):
+    """A paged copy of a linear cache [B, Hkv, cap, D]: the pages go to a
+    seeded random permutation of a pool with extra_pages more pages, which
+    hold NaN bits (a stray read of them would show)."""
+    B, Hkv, cap, D = lin_k.shape
+    n = cap // page_size
+    num = B * n + extra_pages
+    table = np.random.default_rng(seed).permutation(num)[:B * n].reshape(B, n)
+    pools = []
+    for lin in (lin_k, lin_v):
+        pool = torch.full((num, Hkv, page_size, D), float("nan"), dtype=torch.bfloat16)
+        for b in range(B):
+            for i in range(n):
+                pool[table[b, i]] = lin[b, :, i * page_size:(i + 1) * page_size]
+        pools.append(pool)
+    return pools[0], pools[1], torch.as_tensor(table, dtype=torch.int32)
+
+
+def _linear_view(cache):
+    return (torch.from_numpy(O.paged_to_linear(cache.k.cpu().view(torch.int16).numpy(), cache.block_table.cpu().numpy(),
+                                               cache.page_size)).view(torch.bfloat16),
+            torch.from_numpy(O.paged_to_linear(cache.v.cpu().view(torch.int16).numpy(), cache.block_table.cpu().numpy(),
+                                               cache.page_size)).view(torch.bfloat16))
+
+
+@pytest.mark.parametrize("B,cap,page,pos", [
+    (4, 8192, 256, [8191, 3000, 0, 257]),     # ragged positions, 32 pages per sequence
+    (1, 1 << 18, 64, [(1 << 18) - 1]),        # 4096 pages of 64 slots, the per-sequence maximum
+])
+def test_paged_decode_equals_linear_decode(B, cap, page, pos):
+    desc = hb.layer_desc("full")
+    inp = to_dev(synth.decode_inputs(B, 16, 4, seed=101))
+    ck = synth.cache_tensor(B, 4, cap, seed=102)
+    cv = synth.cache_tensor(B, 4, cap, seed=103)
+    kp, vp, table = _paged_from_linear(ck, cv, page, 7, seed=104)
+    # entries of pages past a sequence's position are never read: fill them with junk
+    for b in range(B):
+        table[b, pos[b] // page + 1:] = torch.where(torch.arange(table.shape[1] - pos[b] // page - 1) % 2 == 0,
+                                                    -7, 1 << 30).to(torch.int32)
+    lin = hb.KVCache(ck.to(DEV), cv.to(DEV), "linear")
+    pg = hb.KVCache.paged(kp.to(DEV), vp.to(DEV), table.to(DEV))
+    pos_t = torch.as_tensor(pos, dtype=torch.int32).to(DEV)
+    o_lin = hb.hattn_decode(desc, inp["q"], inp["k"], inp["v"], inp["gate"], pos_t, max(pos), lin)
+    o_pg = hb.hattn_decode(desc, inp["q"], inp["k"], inp["v"], inp["gate"], pos_t, max(pos), pg)
+    torch.cuda.synchronize()
+    assert torch.equal(o_pg, o_lin)
+    dinp = synth.decode_inputs(B, 16, 4, seed=101)
+    ref, _, _ = oracle_decode(desc, dinp, ck, cv, np.array(pos), "linear")
+    check(f"paged decode B={B} cap={cap} page={page}", o_pg.cpu(), ref)
+    # the new rows went to their pages: the paged cache reads back as the linear one
+    for b in range(B):
+        row = pos[b] % page
+        pk = pg.k[int(table[b, pos[b] // page])][:, row].cpu()
+        assert torch.equal(pk, lin.k[b, :, pos[b]].cpu())
+        assert torch.equal(pg.v[int(table[b, pos[b] // page])][:, row].cpu(), lin.v[b, :, pos[b]].cpu())
+
+
+def test_paged_chunked_prefill_equals_linear_prefill():
+    # a 300-token chunk on top of 1000 / 2900 cached tokens, pages of 128
+    B, S, cap, page, starts = 2, 300, 4096, 128, [1000, 2900]
+    desc = hb.layer_desc("full")
+    inp = synth.prefill_inputs(B, S, 16, 4, seed=105)
+    ck = synth.cache_tensor(B, 4, cap, seed=106)
+    cv = synth.cache_tensor(B, 4, cap, seed=107)
+    kp, vp, table = _paged_from_linear(ck, cv, page, 3, seed=108)
+    lin = hb.KVCache(ck.to(DEV), cv.to(DEV), "linear")
+    pg = hb.KVCache.paged(kp.to(DEV), vp.to(DEV), table.to(DEV))
+    d = to_dev(inp)
+    o_lin = hb.hattn_prefill(desc, d["q"], d["k"], d["v"], d["gate"], starts, lin)
+    o_pg = hb.hattn_prefill(desc, d["q"], d["k"], d["v"], d["gate"], starts, pg)
+    torch.cuda.synchronize()
+    assert torch.equal(o_pg, o_lin)
+    lk, lv = _linear_view(pg)
+    assert torch.equal(lk, lin.k.cpu()) and torch.equal(lv, lin.v.cpu())
+    ref, _ = oracle_prefill(desc, inp, ck, cv, starts, "linear", cap)
+    check("paged chunked prefill", o_pg.cpu(), ref)
+
+
 def test_ring_decode_equals_windowed_linear_decode():
     B, p = 4, 3000
     desc = hb.layer_desc("sliding")

@@ -322,6 +322,19 @@ def test_varlen_prefill_sequences_are_independent():
         O.prefill_varlen_ref(q, k, v, g, [0, 5, 4, 15, 15], starts, **kw)
 
 
+def test_paged_to_linear_by_brute_force():
+    # every slot of every sequence, looked up one by one
+    rng = np.random.default_rng(23)
+    B, Hkv, ps, n = 3, 2, 4, 5
+    pool = rng.standard_normal((B * n + 2, Hkv, ps, 3))
+    table = rng.permutation(B * n + 2)[:B * n].reshape(B, n)
+    lin = O.paged_to_linear(pool, table, ps)
+    assert lin.shape == (B, Hkv, n * ps, 3)
+    for b in range(B):
+        for p in range(n * ps):
+            assert np.array_equal(lin[b, :, p], pool[table[b, p // ps], :, p % ps])
+
+
 def test_new_keys_are_cached_as_bf16():
     x = _small_prefill(S=12, seed=6)
     _, kh = O.prefill_ref(x["q"], x["k"], x["v"], x["gate"], [77], window=None, theta=5e6, rotary_fraction=0.25)
