@@ -99,6 +99,52 @@ def copy_calibration():
             "launches": 3}
 
 
+def block_bench(torch, hb, synth, dev, args):
+    """The attention block around the core (RMSNorm, fused q/k/v/g
+    projection, core, out_proj, residual) on the 4B shape with random
+    weights: the full-layer prefill of 8192 tokens and a 64-sequence sliding
+    decode."""
+    S, Hq, Hkv = 8192, 16, 4
+    flops = 4 * 256 * Hq * visible_pairs(S, 0)
+    Hd = 2560
+    bw = {k: v.to(dev) for k, v in synth.block_weights(Hd, Hq, Hkv, seed=60).items()}
+    wts = hb.BlockWeights(bw["norm"], bw["qkvg"], bw["o"], rms_eps=1e-6)
+    xb = synth.hidden_states(S, Hd, seed=61).to(dev)
+    ob = torch.empty_like(xb)
+    cb = hb.KVCache.empty(1, Hkv, S, "linear")
+    dfull = hb.layer_desc("full", Hq, Hkv)
+    n1 = (Hq + 2 * Hkv) * 256 + Hq
+    wsb = torch.empty(hb.block_prefill_workspace_size(dfull, wts, cb, [0, S]), dtype=torch.uint8, device=dev)
+    tb = time_each(torch, lambda: hb.hattn_block_prefill(dfull, wts, xb, [0, S], [0], cb, out=ob, workspace=wsb),
+                   max(args.steps // 2, 5), 2)
+    gemm_fl = 2 * S * Hd * n1 + 2 * S * Hq * 256 * Hd
+    blk_fl = gemm_fl + flops
+    log(f"block prefill (4B, 8192 tokens): {tb['median']:.3f} ms, "
+        f"{blk_fl / (tb['median'] * 1e-3) / 1e12:.1f} TFLOP/s (GEMMs + attention)")
+    Bd = 64
+    pos = synth.positions_uniform(Bd, 512, 1 << 20, seed=0)
+    cr = hb.KVCache(synth.cache_tensor(Bd, Hkv, 512, seed=62, threads=16).to(dev),
+                    synth.cache_tensor(Bd, Hkv, 512, seed=63, threads=16).to(dev), "ring")
+    xd = synth.hidden_states(Bd, Hd, seed=64).to(dev)
+    od = torch.empty_like(xd)
+    dsl = hb.layer_desc("sliding", Hq, Hkv)
+    pos_d = pos.to(torch.int32).to(dev)
+    wsd = torch.empty(hb.block_decode_workspace_size(dsl, wts, cr, Bd), dtype=torch.uint8, device=dev)
+    td = time_each(torch, lambda: hb.hattn_block_decode(dsl, wts, xd, pos_d, int(pos.max()), cr, out=od,
+                                                        workspace=wsd),
+                   max(args.steps, 20), args.warmup)
+    log(f"block decode (4B sliding, batch 64): {td['median'] * 1e3:.1f} us per call")
+    res = {
+        "prefill_s8192_full_ms": {k: round(v, 4) for k, v in tb.items()},
+        "prefill_flop": blk_fl, "prefill_gemm_flop": gemm_fl,
+        "prefill_TFLOP_per_s": round(blk_fl / (tb["median"] * 1e-3) / 1e12, 2),
+        "decode_b64_sliding_us": {k: round(v * 1e3, 2) for k, v in td.items()},
+        "weights": "random, N(0, 0.02^2) projections, RMSNorm weight 1 + N(0, 0.1^2)"}
+    del bw, wts, xb, ob, cb, wsb, cr, xd, od, wsd
+    torch.cuda.empty_cache()
+    return res
+
+
 def to_paged(torch, hb, ck, cv, page, seed):
     """A paged copy of linear caches [B, Hkv, cap, 256]: the B * cap / page
     pages in a seeded random order in one pool, and the block table that
@@ -286,6 +332,8 @@ def run(args):
             "full_layer_ms": {k: round(v, 4) for k, v in tfu.items()}, "full_layer_flop": flf,
             "full_layer_TFLOP_per_s": round(flf / (tfu["median"] * 1e-3) / 1e12, 2)}
 
+        prefill_configs["block_4b"] = block_bench(torch, hb, synth, dev, args)
+
     # ---------------------------------------------------------------- decode
     # Each decode workload is timed as K back-to-back calls (decode kernel and
     # split merge) between one event pair. Calls cycle over enough distinct KV
@@ -387,6 +435,8 @@ def main(argv=None):
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the copy of known size used to scale HBM counters")
+    ap.add_argument("--block-only", action="store_true",
+                    help="only time the attention block around the core (for kernel traces)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); multi-GPU runs are not "
@@ -395,7 +445,14 @@ def main(argv=None):
     if "RANK" in os.environ and os.environ.get("WORLD_SIZE", "1") != "1":
         print("bench.py runs as a single process on one GPU.", file=sys.stderr)
         return 2
-    line = copy_calibration() if args.copy_calibration else run(args)
+    if args.copy_calibration:
+        line = copy_calibration()
+    elif args.block_only:
+        import torch
+        from full_gqa_attention_spark2_amd import binding as hb, synth
+        line = block_bench(torch, hb, synth, torch.device("cuda:0"), args)
+    else:
+        line = run(args)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -54,6 +54,16 @@ class KvCacheC(ctypes.Structure):
     ]
 
 
+class BlockWeightsC(ctypes.Structure):
+    _fields_ = [
+        ("norm_weight", ctypes.c_void_p),
+        ("qkvg_weight", ctypes.c_void_p),
+        ("o_weight", ctypes.c_void_p),
+        ("hidden", ctypes.c_int32),
+        ("rms_eps", ctypes.c_float),
+    ]
+
+
 class KvLayerPlan(ctypes.Structure):
     _fields_ = [
         ("layer_type", ctypes.c_int32),
@@ -85,6 +95,14 @@ _SIGS = {
     "hattn_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc), ctypes.POINTER(KvCacheC), _I]),
     "hattn_decode": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _I, _P, _I,
                                     ctypes.POINTER(KvCacheC), _P, _P, ctypes.c_size_t, _P]),
+    "hattn_block_prefill_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc), ctypes.POINTER(BlockWeightsC),
+                                                             ctypes.POINTER(KvCacheC), _I, _P]),
+    "hattn_block_prefill": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.POINTER(BlockWeightsC), _P, _I, _P, _P,
+                                           ctypes.POINTER(KvCacheC), _P, _P, ctypes.c_size_t, _P]),
+    "hattn_block_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc), ctypes.POINTER(BlockWeightsC),
+                                                            ctypes.POINTER(KvCacheC), _I]),
+    "hattn_block_decode": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.POINTER(BlockWeightsC), _P, _I, _P, _I,
+                                          ctypes.POINTER(KvCacheC), _P, _P, ctypes.c_size_t, _P]),
     "hattn_kv_plan": (ctypes.c_int, [_I, _P, _I, _I, _I, _I, ctypes.POINTER(KvLayerPlan),
                                      ctypes.POINTER(ctypes.c_uint64)]),
     "hattn_kv_cache_at": (ctypes.c_int, [ctypes.POINTER(KvLayerPlan), _P, ctypes.POINTER(KvCacheC)]),
@@ -302,6 +320,78 @@ def hattn_decode(desc, q, k, v, gate, pos, max_pos, cache, out=None, workspace=N
     _check("hattn_decode", lib().hattn_decode(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), B, _ptr(pos), int(max_pos),
         ctypes.byref(cc), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(q.device)))
+    return out
+
+
+class BlockWeights:
+    """Weights of one attention block on the GPU (bf16): the input RMSNorm
+    weight [hidden], the fused projection [(Hq + 2 Hkv) * 256 + Hq, hidden]
+    (q_k_v_proj rows Q, K, V, then the g_proj rows) and out_proj [hidden,
+    Hq * 256]."""
+
+    def __init__(self, norm_weight, qkvg_weight, o_weight, rms_eps=1e-6):
+        H = norm_weight.shape[0]
+        _need(norm_weight, "norm_weight", shape=(H,))
+        _need(qkvg_weight, "qkvg_weight")
+        _need(o_weight, "o_weight")
+        if qkvg_weight.dim() != 2 or qkvg_weight.shape[1] != H or o_weight.dim() != 2 or o_weight.shape[0] != H:
+            raise ValueError("weight shapes do not match the hidden size")
+        self.norm_weight, self.qkvg_weight, self.o_weight = norm_weight, qkvg_weight, o_weight
+        self.hidden, self.rms_eps = H, float(rms_eps)
+
+    def c(self) -> BlockWeightsC:
+        return BlockWeightsC(self.norm_weight.data_ptr(), self.qkvg_weight.data_ptr(), self.o_weight.data_ptr(),
+                             self.hidden, self.rms_eps)
+
+
+def block_prefill_workspace_size(desc, weights, cache, cu_seqlens):
+    B = len(cu_seqlens) - 1
+    cu = (ctypes.c_int32 * (B + 1))(*[int(v) for v in cu_seqlens])
+    cc, wc = cache.c(), weights.c()
+    return int(lib().hattn_block_prefill_workspace_size(ctypes.byref(desc), ctypes.byref(wc), ctypes.byref(cc), B,
+                                                        ctypes.cast(cu, ctypes.c_void_p)))
+
+
+def block_decode_workspace_size(desc, weights, cache, B):
+    cc, wc = cache.c(), weights.c()
+    return int(lib().hattn_block_decode_workspace_size(ctypes.byref(desc), ctypes.byref(wc), ctypes.byref(cc), B))
+
+
+def hattn_block_prefill(desc, weights, x, cu_seqlens, start_pos, cache, out=None, workspace=None):
+    """The attention block over packed new tokens x [T, hidden] (host
+    cu_seqlens [B+1], start positions [B]); returns out [T, hidden] =
+    x + out_proj(core(...)); out may be x."""
+    T, H = x.shape
+    B = len(cu_seqlens) - 1
+    _need(x, "x", shape=(T, weights.hidden))
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", shape=x.shape)
+    cu = (ctypes.c_int32 * (B + 1))(*[int(v) for v in cu_seqlens])
+    sp = (ctypes.c_int32 * B)(*[int(v) for v in start_pos])
+    cc, wc = cache.c(), weights.c()
+    ws = _workspace(block_prefill_workspace_size(desc, weights, cache, cu_seqlens), x.device, workspace)
+    _check("hattn_block_prefill", lib().hattn_block_prefill(
+        ctypes.byref(desc), ctypes.byref(wc), _ptr(x), B, ctypes.cast(cu, ctypes.c_void_p),
+        ctypes.cast(sp, ctypes.c_void_p), ctypes.byref(cc), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(x.device)))
+    return out
+
+
+def hattn_block_decode(desc, weights, x, pos, max_pos, cache, out=None, workspace=None):
+    """The attention block for one token per sequence, x [B, hidden], at
+    device int32 positions pos [B]; returns out [B, hidden]; out may be x."""
+    B, H = x.shape
+    _need(x, "x", shape=(B, weights.hidden))
+    _need(pos, "pos", torch.int32, (B,))
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", shape=x.shape)
+    cc, wc = cache.c(), weights.c()
+    ws = _workspace(block_decode_workspace_size(desc, weights, cache, B), x.device, workspace)
+    _check("hattn_block_decode", lib().hattn_block_decode(
+        ctypes.byref(desc), ctypes.byref(wc), _ptr(x), B, _ptr(pos), int(max_pos), ctypes.byref(cc), _ptr(out),
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(x.device)))
     return out
 
 

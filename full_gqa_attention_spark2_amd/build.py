@@ -18,7 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhattn.so")
-SOURCES = ["hattn_api.cpp", "hattn_plan.cpp", "hattn_rope.hip", "hattn_prefill.hip", "hattn_decode.hip"]
+SOURCES = ["hattn_api.cpp", "hattn_plan.cpp", "hattn_block.cpp", "hattn_rope.hip", "hattn_prefill.hip",
+           "hattn_decode.hip", "hattn_norm.hip"]
 ARCH = "gfx950"
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
@@ -52,7 +53,8 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-L/opt/rocm/lib", "-lhipblaslt",
+           "-Wl,-rpath,/opt/rocm/lib"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

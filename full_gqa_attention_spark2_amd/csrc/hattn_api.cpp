@@ -269,15 +269,30 @@ size_t hattn_prefill_varlen_workspace_size(const hattn_layer_desc* desc, const h
   return prefill_layout(desc, cache, batch, cu_seqlens[batch], max_len).total;
 }
 
-namespace {
+}  // extern "C"
+
+namespace hattn {
+
+size_t prefill_workspace_bytes(const hattn_layer_desc* desc, const hattn_kv_cache* cache, int batch,
+                               long long total_tokens, int max_len) {
+  return prefill_layout(desc, cache, batch, total_tokens, max_len).total;
+}
+
+size_t decode_workspace_bytes(const hattn_layer_desc* desc, const hattn_kv_cache* cache, int batch) {
+  return hattn_decode_workspace_size(desc, cache, batch);
+}
 
 // One prefill call over packed new tokens: sequence b's tokens are rows
 // tok0[b] .. tok0[b] + len[b] - 1 of q/k/v/gate/out, at positions
 // start_pos[b] + 0 .. len[b] - 1.
+// Token rows of q, k/v and gate are q_stride, kv_stride and gate_stride
+// elements apart (dense: Hq * 256, Hkv * 256, Hq).
 int prefill_packed(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
                    const void* gate, int32_t batch, const int* tok0, const int* len, long long total,
                    const int32_t* start_pos, const hattn_kv_cache* cache, void* out, void* workspace,
-                   size_t workspace_bytes, hipStream_t stream) {
+                   size_t workspace_bytes, hipStream_t stream, long long q_stride, long long kv_stride,
+                   long long gate_stride) {
+  if (batch > kMaxPrefillBatch) return HATTN_ERR_UNSUPPORTED;
   const bool ring = cache->kind == HATTN_KV_RING;
   int max_len = 0;
   for (int b = 0; b < batch; ++b) {
@@ -334,6 +349,7 @@ int prefill_packed(const hattn_layer_desc* desc, const void* q, const void* k, c
   PrefillPrepArgs ra{};
   ra.k = (const uint16_t*)k;
   ra.v = (const uint16_t*)v;
+  ra.kv_stride = kv_stride;
   ra.table = table;
   ra.dst_k = ring ? stage_k : (uint16_t*)cache->k;
   ra.dst_v = ring ? stage_v : (uint16_t*)cache->v;
@@ -368,6 +384,8 @@ int prefill_packed(const hattn_layer_desc* desc, const void* q, const void* k, c
 
   // 3. attention over the linear key rows (queries rotated in the kernel)
   aa.q = (const uint16_t*)q;
+  aa.q_stride = q_stride;
+  aa.gate_stride = gate_stride;
   aa.table = table;
   aa.kc = ring ? stage_k : (const uint16_t*)cache->k;
   aa.vc = ring ? stage_v : (const uint16_t*)cache->v;
@@ -390,6 +408,10 @@ int prefill_packed(const hattn_layer_desc* desc, const void* q, const void* k, c
   return HATTN_OK;
 }
 
+}  // namespace hattn
+
+namespace {
+
 // Checks shared by both prefill entry points (before any sequence data).
 int prefill_common_checks(const hattn_layer_desc* desc, const hattn_kv_cache* cache, int32_t batch,
                           const int32_t* start_pos) {
@@ -404,6 +426,8 @@ int prefill_common_checks(const hattn_layer_desc* desc, const hattn_kv_cache* ca
 }
 
 }  // namespace
+
+extern "C" {
 
 int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
                   const void* gate, int32_t batch, int32_t seq_len, const int32_t* start_pos,
@@ -421,7 +445,8 @@ int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k, co
     len[b] = seq_len;
   }
   return prefill_packed(desc, q, k, v, gate, batch, tok0, len, (long long)batch * seq_len, start_pos,
-                        cache, out, workspace, workspace_bytes, stream);
+                        cache, out, workspace, workspace_bytes, stream, (long long)desc->num_q_heads * kHeadDimSupported,
+                        (long long)desc->num_kv_heads * kHeadDimSupported, desc->num_q_heads);
 }
 
 int hattn_prefill_varlen(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
@@ -439,7 +464,8 @@ int hattn_prefill_varlen(const hattn_layer_desc* desc, const void* q, const void
     len[b] = cu_seqlens[b + 1] - cu_seqlens[b];
   }
   return prefill_packed(desc, q, k, v, gate, batch, tok0, len, cu_seqlens[batch], start_pos, cache, out,
-                        workspace, workspace_bytes, stream);
+                        workspace, workspace_bytes, stream, (long long)desc->num_q_heads * kHeadDimSupported,
+                        (long long)desc->num_kv_heads * kHeadDimSupported, desc->num_q_heads);
 }
 
 size_t hattn_decode_workspace_size(const hattn_layer_desc* desc, const hattn_kv_cache* cache,
@@ -454,10 +480,16 @@ size_t hattn_decode_workspace_size(const hattn_layer_desc* desc, const hattn_kv_
   return align_up(parts * desc->head_dim * 4, 256) + align_up(parts * 2 * 4, 256);
 }
 
-int hattn_decode(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
-                 const void* gate, int32_t batch, const int32_t* pos, int32_t max_pos,
-                 const hattn_kv_cache* cache, void* out, void* workspace, size_t workspace_bytes,
-                 hipStream_t stream) {
+}  // extern "C"
+
+namespace hattn {
+
+// hattn_decode with sequence rows of q, k/v and gate q_stride, kv_stride and
+// gate_stride elements apart (dense: Hq * 256, Hkv * 256, Hq).
+int decode_strided(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
+                   const void* gate, int32_t batch, const int32_t* pos, int32_t max_pos,
+                   const hattn_kv_cache* cache, void* out, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream, long long q_stride, long long kv_stride, long long gate_stride) {
   int st = check_desc(desc);
   if (st != HATTN_OK) return st;
   if (batch <= 0) return HATTN_ERR_SHAPE;
@@ -482,6 +514,9 @@ int hattn_decode(const hattn_layer_desc* desc, const void* q, const void* k, con
   a.k = (const uint16_t*)k;
   a.v = (const uint16_t*)v;
   a.gate = (const uint16_t*)gate;
+  a.q_stride = q_stride;
+  a.kv_stride = kv_stride;
+  a.gate_stride = gate_stride;
   a.pos = pos;
   a.kc = (uint16_t*)cache->k;
   a.vc = (uint16_t*)cache->v;
@@ -505,6 +540,21 @@ int hattn_decode(const hattn_layer_desc* desc, const void* q, const void* k, con
   const hipError_t e = launch_decode(a, stream);
   profile_end(prof, stream);
   return from_hip(e);
+}
+
+}  // namespace hattn
+
+extern "C" {
+
+int hattn_decode(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
+                 const void* gate, int32_t batch, const int32_t* pos, int32_t max_pos,
+                 const hattn_kv_cache* cache, void* out, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+  const int st = check_desc(desc);
+  if (st != HATTN_OK) return st;
+  return decode_strided(desc, q, k, v, gate, batch, pos, max_pos, cache, out, workspace, workspace_bytes,
+                        stream, (long long)desc->num_q_heads * kHeadDimSupported,
+                        (long long)desc->num_kv_heads * kHeadDimSupported, desc->num_q_heads);
 }
 
 int hattn_profile_enable(int enable) {

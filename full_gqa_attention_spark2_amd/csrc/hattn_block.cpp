@@ -1,0 +1,235 @@
+// The attention block around the core (page "Spark-X2.5 架构（4B / 1.7B）",
+// §2 figure 1: RMSNorm -> q_k_v_proj and g_proj -> RoPE and attention ->
+// per-head gate -> out_proj -> + residual). The two projections are plain
+// GEMMs and run on hipBLASLt; the norm, the core and the residual add are
+// this library's kernels.
+#include <stdint.h>
+
+#include <map>
+#include <mutex>
+#include <tuple>
+
+#include <hipblaslt/hipblaslt.h>
+
+#include "hattn.h"
+#include "hattn_internal.h"
+
+using namespace hattn;
+
+namespace {
+
+constexpr size_t kGemmWorkspace = 32u << 20;  // hipBLASLt workspace per GEMM
+constexpr int kGemmCandidates = 16;           // heuristic results considered
+constexpr int kMaxDevices = 64;
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+std::mutex g_mu;
+hipblasLtHandle_t g_handle[kMaxDevices];
+
+hipblasLtHandle_t lt_handle() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!g_handle[dev] && hipblasLtCreate(&g_handle[dev]) != HIPBLAS_STATUS_SUCCESS) g_handle[dev] = nullptr;
+  return g_handle[dev];
+}
+
+// One row-major GEMM, D[T][N] = A[T][K] W[N][K]^T, bf16 in and out, fp32
+// accumulate. In hipBLASLt's column-major terms: D^T (N x T, ld ldd) =
+// op_T(W^T: K x N, ld K) * A^T (K x T, ld lda).
+struct GemmPlan {
+  hipblasLtMatmulDesc_t op = nullptr;
+  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, ld = nullptr;
+  hipblasLtMatmulAlgo_t algo{};
+  bool ok = false;
+};
+std::map<std::tuple<int, int, int, long long, long long, int>, GemmPlan> g_plans;
+
+const GemmPlan* gemm_plan(hipblasLtHandle_t h, int N, int K, int T, long long lda, long long ldd) {
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  std::lock_guard<std::mutex> lock(g_mu);
+  const auto key = std::make_tuple(N, K, T, lda, ldd, dev);
+  auto it = g_plans.find(key);
+  if (it != g_plans.end()) return it->second.ok ? &it->second : nullptr;
+  GemmPlan p;
+  bool ok = hipblasLtMatmulDescCreate(&p.op, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS;
+  const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
+  ok = ok && hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta)) == HIPBLAS_STATUS_SUCCESS;
+  ok = ok && hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb)) == HIPBLAS_STATUS_SUCCESS;
+  ok = ok && hipblasLtMatrixLayoutCreate(&p.la, HIP_R_16BF, K, N, K) == HIPBLAS_STATUS_SUCCESS;
+  ok = ok && hipblasLtMatrixLayoutCreate(&p.lb, HIP_R_16BF, K, T, lda) == HIPBLAS_STATUS_SUCCESS;
+  ok = ok && hipblasLtMatrixLayoutCreate(&p.ld, HIP_R_16BF, N, T, ldd) == HIPBLAS_STATUS_SUCCESS;
+  if (ok) {
+    hipblasLtMatmulPreference_t pref = nullptr;
+    const uint64_t ws = kGemmWorkspace;
+    ok = hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS &&
+         hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &ws, sizeof(ws)) ==
+             HIPBLAS_STATUS_SUCCESS;
+    // the best-ranked algorithm that fits the workspace (the ranking does not
+    // always honour the workspace preference)
+    hipblasLtMatmulHeuristicResult_t res[kGemmCandidates];
+    int n = 0;
+    ok = ok && hipblasLtMatmulAlgoGetHeuristic(h, p.op, p.la, p.lb, p.ld, p.ld, pref, kGemmCandidates, res, &n) ==
+                   HIPBLAS_STATUS_SUCCESS;
+    int pick = -1;
+    for (int i = 0; ok && i < n && pick < 0; ++i)
+      if (res[i].state == HIPBLAS_STATUS_SUCCESS && res[i].workspaceSize <= kGemmWorkspace) pick = i;
+    ok = ok && pick >= 0;
+    if (ok) p.algo = res[pick].algo;
+    if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+  }
+  p.ok = ok;
+  return (g_plans[key] = p).ok ? &g_plans[key] : nullptr;
+}
+
+int gemm(const void* W, int N, int K, const void* A, int T, long long lda, void* D, long long ldd, void* ws,
+         hipStream_t s) {
+  if (T == 0) return HATTN_OK;
+  hipblasLtHandle_t h = lt_handle();
+  if (!h) return HATTN_ERR_LAUNCH;
+  const GemmPlan* p = gemm_plan(h, N, K, T, lda, ldd);
+  if (!p) return HATTN_ERR_LAUNCH;
+  const float alpha = 1.f, beta = 0.f;
+  return hipblasLtMatmul(h, p->op, &alpha, W, p->la, A, p->lb, &beta, D, p->ld, D, p->ld, &p->algo, ws,
+                         kGemmWorkspace, s) == HIPBLAS_STATUS_SUCCESS
+             ? HATTN_OK
+             : HATTN_ERR_LAUNCH;
+}
+
+int check_weights(const hattn_layer_desc* d, const hattn_block_weights* w) {
+  if (!d || !w) return HATTN_ERR_NULL;
+  if (!w->norm_weight || !w->qkvg_weight || !w->o_weight) return HATTN_ERR_NULL;
+  if (w->hidden <= 0 || w->hidden % 8 || !(w->rms_eps > 0.f)) return HATTN_ERR_SHAPE;
+  if (((uintptr_t)w->norm_weight | (uintptr_t)w->qkvg_weight | (uintptr_t)w->o_weight) & 15u) return HATTN_ERR_ALIGN;
+  return HATTN_OK;
+}
+
+// Workspace of one block call over T tokens: h [T][hidden], the fused
+// projection [T][N1], the core's output [T][Hq*256], the out_proj result
+// [T][hidden], the GEMM workspace, then the core's own workspace.
+struct BlockLayout {
+  size_t h, qkvg, attn, y, gemm, core_off, total;
+};
+BlockLayout block_layout(const hattn_layer_desc* d, const hattn_block_weights* w, long long T, size_t core) {
+  BlockLayout L{};
+  const long long n1 = (long long)(d->num_q_heads + 2 * d->num_kv_heads) * 256 + d->num_q_heads;
+  L.h = 0;
+  L.qkvg = L.h + align256((size_t)T * w->hidden * 2);
+  L.attn = L.qkvg + align256((size_t)T * n1 * 2);
+  L.y = L.attn + align256((size_t)T * d->num_q_heads * 256 * 2);
+  L.gemm = L.y + align256((size_t)T * w->hidden * 2);
+  L.core_off = L.gemm + kGemmWorkspace;
+  L.total = L.core_off + core;
+  return L;
+}
+
+// The shared block pipeline around `core` (a callable that runs the core on
+// the projections); T tokens.
+template <class Core>
+int block_run(const hattn_layer_desc* desc, const hattn_block_weights* w, const void* x, long long T,
+              void* out, char* ws, const BlockLayout& L, hipStream_t s, Core core) {
+  const int Hq = desc->num_q_heads, Hkv = desc->num_kv_heads, H = w->hidden;
+  const long long n1 = (long long)(Hq + 2 * Hkv) * 256 + Hq;
+  uint16_t* h = (uint16_t*)(ws + L.h);
+  uint16_t* qkvg = (uint16_t*)(ws + L.qkvg);
+  uint16_t* attn = (uint16_t*)(ws + L.attn);
+  uint16_t* y = (uint16_t*)(ws + L.y);
+  RmsNormArgs na{};
+  na.x = (const uint16_t*)x;
+  na.w = (const uint16_t*)w->norm_weight;
+  na.y = h;
+  na.T = (int)T;
+  na.H = H;
+  na.eps = w->rms_eps;
+  if (launch_rms_norm(na, s) != hipSuccess) return HATTN_ERR_LAUNCH;
+  int st = gemm(w->qkvg_weight, (int)n1, H, h, (int)T, H, qkvg, n1, ws + L.gemm, s);
+  if (st != HATTN_OK) return st;
+  st = core(qkvg, qkvg + (size_t)Hq * 256, qkvg + (size_t)(Hq + Hkv) * 256, qkvg + (size_t)(Hq + 2 * Hkv) * 256,
+            n1, attn);
+  if (st != HATTN_OK) return st;
+  st = gemm(w->o_weight, H, Hq * 256, attn, (int)T, (long long)Hq * 256, y, H, ws + L.gemm, s);
+  if (st != HATTN_OK) return st;
+  return launch_residual_add((const uint16_t*)x, y, (uint16_t*)out, T * H, s) == hipSuccess ? HATTN_OK
+                                                                                           : HATTN_ERR_LAUNCH;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+size_t hattn_block_prefill_workspace_size(const hattn_layer_desc* desc, const hattn_block_weights* w,
+                                          const hattn_kv_cache* cache, int32_t batch, const int32_t* cu_seqlens) {
+  if (check_weights(desc, w) != HATTN_OK || !cache || batch <= 0 || !cu_seqlens || cu_seqlens[0] != 0) return 0;
+  int max_len = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (cu_seqlens[b + 1] < cu_seqlens[b]) return 0;
+    max_len = std::max(max_len, cu_seqlens[b + 1] - cu_seqlens[b]);
+  }
+  const long long T = cu_seqlens[batch];
+  return block_layout(desc, w, T, prefill_workspace_bytes(desc, cache, batch, T, max_len)).total;
+}
+
+int hattn_block_prefill(const hattn_layer_desc* desc, const hattn_block_weights* w, const void* x, int32_t batch,
+                        const int32_t* cu_seqlens, const int32_t* start_pos, const hattn_kv_cache* cache,
+                        void* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_weights(desc, w);
+  if (st != HATTN_OK) return st;
+  if (batch <= 0) return HATTN_ERR_SHAPE;
+  if (batch > kMaxPrefillBatch) return HATTN_ERR_UNSUPPORTED;
+  if (!cu_seqlens || !start_pos || !cache) return HATTN_ERR_NULL;
+  if (cu_seqlens[0] != 0) return HATTN_ERR_SHAPE;
+  int tok0[kMaxPrefillBatch], len[kMaxPrefillBatch], max_len = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (cu_seqlens[b + 1] < cu_seqlens[b]) return HATTN_ERR_SHAPE;
+    tok0[b] = cu_seqlens[b];
+    len[b] = cu_seqlens[b + 1] - cu_seqlens[b];
+    max_len = std::max(max_len, len[b]);
+  }
+  const long long T = cu_seqlens[batch];
+  if (T == 0) return HATTN_OK;
+  if (!x || !out) return HATTN_ERR_NULL;
+  if (!aligned16(x) || !aligned16(out) || !aligned16(workspace)) return HATTN_ERR_ALIGN;
+  const size_t core_bytes = prefill_workspace_bytes(desc, cache, batch, T, max_len);
+  const BlockLayout L = block_layout(desc, w, T, core_bytes);
+  if (!workspace || workspace_bytes < L.total) return HATTN_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  return block_run(desc, w, x, T, out, ws, L, stream,
+                   [&](const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g, long long ld,
+                       uint16_t* attn) {
+                     return prefill_packed(desc, q, k, v, g, batch, tok0, len, T, start_pos, cache, attn,
+                                           ws + L.core_off, core_bytes, stream, ld, ld, ld);
+                   });
+}
+
+size_t hattn_block_decode_workspace_size(const hattn_layer_desc* desc, const hattn_block_weights* w,
+                                         const hattn_kv_cache* cache, int32_t batch) {
+  if (check_weights(desc, w) != HATTN_OK || !cache || batch <= 0) return 0;
+  return block_layout(desc, w, batch, decode_workspace_bytes(desc, cache, batch)).total;
+}
+
+int hattn_block_decode(const hattn_layer_desc* desc, const hattn_block_weights* w, const void* x, int32_t batch,
+                       const int32_t* pos, int32_t max_pos, const hattn_kv_cache* cache, void* out, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  int st = check_weights(desc, w);
+  if (st != HATTN_OK) return st;
+  if (batch <= 0) return HATTN_ERR_SHAPE;
+  if (!cache) return HATTN_ERR_NULL;
+  if (!x || !out) return HATTN_ERR_NULL;
+  if (!aligned16(x) || !aligned16(out) || !aligned16(workspace)) return HATTN_ERR_ALIGN;
+  const size_t core_bytes = decode_workspace_bytes(desc, cache, batch);
+  const BlockLayout L = block_layout(desc, w, batch, core_bytes);
+  if (!workspace || workspace_bytes < L.total) return HATTN_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  return block_run(desc, w, x, batch, out, ws, L, stream,
+                   [&](const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g, long long ld,
+                       uint16_t* attn) {
+                     return decode_strided(desc, q, k, v, g, batch, pos, max_pos, cache, attn, ws + L.core_off,
+                                           core_bytes, stream, ld, ld, ld);
+                   });
+}
+
+}  // extern "C"

@@ -109,7 +109,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   uint16_t gate_bits[kGroup];
 #pragma unroll
   for (int hh = 0; hh < kGroup; ++hh)
-    gate_bits[hh] = a.nsplit == 1 ? a.gate[(size_t)b * a.Hq + kvh * kGroup + hh] : 0;
+    gate_bits[hh] = a.nsplit == 1 ? a.gate[(size_t)b * a.gate_stride + kvh * kGroup + hh] : 0;
 
   // ---- the token's inputs, one DMA instruction per wave
   {
@@ -117,16 +117,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     uint32_t bytes, voff = 16u * lane;
     void* dst;
     if (wave < 2) {
-      src = a.q + ((size_t)b * a.Hq + kvh * kGroup) * kHeadDim;
+      src = a.q + (size_t)b * a.q_stride + (size_t)kvh * kGroup * kHeadDim;
       bytes = kGroup * kHeadDim * 2;
       voff += 1024u * wave;
       dst = (char*)q_stage + 1024 * wave;
     } else if (wave == 2) {
-      src = a.k + ((size_t)b * a.Hkv + kvh) * kHeadDim;
+      src = a.k + (size_t)b * a.kv_stride + (size_t)kvh * kHeadDim;
       bytes = kHeadDim * 2;
       dst = kv_stage[0];
     } else {
-      src = a.v + ((size_t)b * a.Hkv + kvh) * kHeadDim;
+      src = a.v + (size_t)b * a.kv_stride + (size_t)kvh * kHeadDim;
       bytes = kHeadDim * 2;
       dst = kv_stage[1];
     }
@@ -515,7 +515,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   __syncthreads();
   if (g == 0) {
     const float O = ((acc + part[0][d]) + part[1][d]) + part[2][d];
-    const float gl = bf16_bits_to_float(a.gate[(size_t)b * a.Hq + h]);
+    const float gl = bf16_bits_to_float(a.gate[(size_t)b * a.gate_stride + h]);
     o[d] = float_to_bf16_bits(O / L * gate_factor(gl, a.gate_act));
   }
 }

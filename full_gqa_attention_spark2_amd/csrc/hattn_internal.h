@@ -30,8 +30,9 @@ struct PagedKv {
 // New tokens are packed: sequence b's token i is row tok0[b] + i of k, v
 // and the table, for i < len[b].
 struct PrefillPrepArgs {
-  const uint16_t* k;      // bf16 [T][Hkv][256]
+  const uint16_t* k;      // bf16 [T][Hkv][256], token rows kv_stride elements apart
   const uint16_t* v;
+  long long kv_stride;    // Hkv * 256 when dense
   float2* table;          // [T][r/2] (cos, sin)
   uint16_t* dst_k;
   uint16_t* dst_v;
@@ -63,7 +64,9 @@ struct RingCopyArgs {
 
 // Queries are packed like the new tokens of PrefillPrepArgs.
 struct PrefillAttnArgs {
-  const uint16_t* q;      // bf16 [T][Hq][256], before RoPE
+  const uint16_t* q;      // bf16 [T][Hq][256], before RoPE; token rows q_stride apart
+  long long q_stride;     // Hq * 256 when dense
+  long long gate_stride;  // Hq when dense
   const float2* table;    // [T][r/2] cos/sin of the query positions
   const uint16_t* kc;     // bf16 [B][Hkv][rows][256], rotated keys (or a paged pool)
   const uint16_t* vc;
@@ -87,6 +90,9 @@ struct DecodeArgs {
   const uint16_t* q;      // bf16 [B][Hq][256]
   const uint16_t* k;      // bf16 [B][Hkv][256]
   const uint16_t* v;
+  long long q_stride;     // elements between sequences' rows of q (Hq * 256 when dense),
+  long long kv_stride;    //   of k and v (Hkv * 256), and of gate (Hq)
+  long long gate_stride;
   const uint16_t* gate;   // bf16 [B][Hq]
   const int* pos;         // int32 [B], device
   uint16_t* kc;           // cache [B][Hkv][cap][256] (or a paged pool)
@@ -117,6 +123,15 @@ struct ProbeArgs {
   int ring, cap, window, q_pos0, n_q;
 };
 
+// Input RMSNorm of the attention block: y[t] = bf16(w * x[t] / rms(x[t])).
+struct RmsNormArgs {
+  const uint16_t* x;  // bf16 [T][H]
+  const uint16_t* w;  // bf16 [H]
+  uint16_t* y;        // bf16 [T][H]
+  int T, H;           // H a multiple of 8
+  float eps;
+};
+
 // Kernel arguments travel by value; keep each struct within 4 KiB.
 static_assert(sizeof(PrefillPrepArgs) <= 4096, "kernel argument size");
 static_assert(sizeof(RingCopyArgs) <= 4096, "kernel argument size");
@@ -124,11 +139,37 @@ static_assert(sizeof(PrefillAttnArgs) <= 4096, "kernel argument size");
 static_assert(sizeof(DecodeArgs) <= 4096, "kernel argument size");
 static_assert(sizeof(RopeApplyArgs) <= 4096, "kernel argument size");
 
+}  // namespace hattn
+
+#include "hattn.h"
+
+namespace hattn {
+
+// The C-ABI prefill over packed new tokens (sequence b: rows tok0[b] ..
+// tok0[b] + len[b] - 1) and decode, with token rows of q, k/v and gate
+// q_stride, kv_stride and gate_stride elements apart. Validation as in the
+// public entry points; return a hattn_status.
+int prefill_packed(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
+                   const void* gate, int32_t batch, const int* tok0, const int* len, long long total,
+                   const int32_t* start_pos, const hattn_kv_cache* cache, void* out, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream, long long q_stride, long long kv_stride,
+                   long long gate_stride);
+int decode_strided(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
+                   const void* gate, int32_t batch, const int32_t* pos, int32_t max_pos,
+                   const hattn_kv_cache* cache, void* out, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream, long long q_stride, long long kv_stride, long long gate_stride);
+// Workspace bytes of prefill_packed / decode_strided.
+size_t prefill_workspace_bytes(const hattn_layer_desc* desc, const hattn_kv_cache* cache, int batch,
+                               long long total_tokens, int max_len);
+size_t decode_workspace_bytes(const hattn_layer_desc* desc, const hattn_kv_cache* cache, int batch);
+
 hipError_t launch_prefill_prep(const PrefillPrepArgs& a, hipStream_t s);
 hipError_t launch_ring_to_stage(const RingCopyArgs& a, hipStream_t s);
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_rope_apply(const RopeApplyArgs& a, hipStream_t s);
 hipError_t launch_index_probe(const ProbeArgs& a, hipStream_t s);
+hipError_t launch_rms_norm(const RmsNormArgs& a, hipStream_t s);
+hipError_t launch_residual_add(const uint16_t* x, const uint16_t* y, uint16_t* out, long long n, hipStream_t s);
 
 }  // namespace hattn

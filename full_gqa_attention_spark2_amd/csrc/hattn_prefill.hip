@@ -243,12 +243,12 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   const int qrow = q0 + (lane & 31);
   const bool qvalid = qrow < len;
   // the gate logit, requested now and used in the epilogue
-  const size_t orow = (tok0 + (qvalid ? qrow : len - 1)) * a.Hq + h;
+  const size_t orow = (tok0 + (qvalid ? qrow : len - 1)) * (size_t)a.gate_stride + h;
   const uint16_t gate_bits = a.gate[orow];
   bf16x8 qf[16];
   {
     const int qr = qvalid ? qrow : len - 1;
-    const uint16_t* qp = a.q + ((tok0 + qr) * a.Hq + h) * kHeadDim;
+    const uint16_t* qp = a.q + (tok0 + qr) * (size_t)a.q_stride + (size_t)h * kHeadDim;
     const int half = a.r >> 1;
     const float2* tp = a.table + (tok0 + qr) * half;
     // With r a multiple of 32 (the pages' 64 and 256), the partner of

@@ -34,7 +34,9 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(PrefillPrepA
   const int ring_from = len - min(len, a.ring_cap);
 
   // chunk c: token c / (32 Hkv), head (c / 32) % Hkv, channels 8(c % 32) .. +7
-  auto src_off = [&](int c) { return ((row0 + c / (a.Hkv * 32)) * a.Hkv + (c >> 5) % a.Hkv) * kHeadDim; };
+  auto src_off = [&](int c) {
+    return (row0 + c / (a.Hkv * 32)) * (size_t)a.kv_stride + (size_t)((c >> 5) % a.Hkv) * kHeadDim;
+  };
   auto partner = [&](int ch) {  // chunk holding the RoPE partners of chunk ch
     const int d0 = ch * 8;
     return d0 < a.r ? (d0 < half ? d0 + half : d0 - half) >> 3 : ch;

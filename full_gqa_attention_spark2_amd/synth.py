@@ -93,3 +93,23 @@ def positions_uniform(B, lo, hi, seed=0):
     """int32 positions uniform in [lo, hi)."""
     g = _gen(seed)
     return torch.randint(int(lo), int(hi), (B,), generator=g, dtype=torch.int64).to(torch.int32)
+
+
+WEIGHT_STD = 0.02   # projection weights ~ N(0, 0.02^2), a common initialiser scale
+NORM_JITTER = 0.1   # RMSNorm weights ~ 1 + N(0, 0.1^2)
+
+
+def block_weights(hidden, Hq, Hkv, D=256, seed=0):
+    """Random weights of one attention block, CPU bf16: the RMSNorm weight
+    [hidden], the fused q/k/v/g projection [(Hq + 2 Hkv) D + Hq, hidden] and
+    out_proj [hidden, Hq D]. Draw order: norm, fused projection, out_proj."""
+    g = _gen(seed)
+    norm = (1.0 + NORM_JITTER * torch.randn(hidden, generator=g)).to(torch.bfloat16)
+    qkvg = _normal(g, ((Hq + 2 * Hkv) * D + Hq, hidden), WEIGHT_STD)
+    o = _normal(g, (hidden, Hq * D), WEIGHT_STD)
+    return {"norm": norm, "qkvg": qkvg, "o": o}
+
+
+def hidden_states(T, hidden, seed=0):
+    """Block inputs x [T, hidden] ~ N(0, 1), bf16."""
+    return _normal(_gen(seed), (T, hidden))

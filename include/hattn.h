@@ -22,7 +22,9 @@
  *   - Tensors are caller-owned device memory (bf16 unless stated), dense,
  *     row-major in the layouts given below, 16-byte aligned.
  *   - The library allocates no device memory and keeps no state beyond the
- *     profiling events below. Every call only enqueues work on `stream`
+ *     profiling events below, except that the attention-block entry points
+ *     create one hipBLASLt handle per device on first use and cache their
+ *     GEMM plans. Every call only enqueues work on `stream`
  *     (NULL = the default stream); results are valid after the stream
  *     synchronises.
  *   - Return value: HATTN_OK (0) or a negative hattn_status; arguments are
@@ -207,6 +209,62 @@ int hattn_decode(const hattn_layer_desc* desc, const void* q, const void* k,
                  const int32_t* pos, int32_t max_pos,
                  const hattn_kv_cache* cache, void* out, void* workspace,
                  size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * The attention block around the core (page §2 figure 1, the decoder
+ * layer's dataflow; §1 config table; §3; §5): with x the block input,
+ *   h = RMSNorm(x)                     fp32, times the weight, cast to bf16
+ *   [q | k | v | g] = h W_qkvg^T       q_k_v_proj and g_proj, bf16 outputs
+ *   a = attention core(q, k, v, g)     as hattn_prefill_varlen / hattn_decode
+ *   out = x + a W_o^T                  out_proj (bf16), then the residual add
+ *                                      in fp32 with one bf16 rounding
+ * Linear layers have no bias (page §5: attention_bias false). The GEMMs run
+ * on hipBLASLt (bf16 in and out, fp32 accumulate) through one handle per
+ * device, created on first use; the other steps are this library's kernels.
+ */
+typedef struct {
+  const void* norm_weight;  /* bf16 [hidden]: the input RMSNorm's weight    */
+  const void* qkvg_weight;  /* bf16 [(num_q_heads + 2 num_kv_heads) * 256 +
+                               num_q_heads][hidden]: the q_k_v_proj rows (Q,
+                               then K, then V; 6144 on the 4B shape) followed
+                               by the g_proj rows (one per query head)       */
+  const void* o_weight;     /* bf16 [hidden][num_q_heads * 256]: out_proj    */
+  int32_t hidden;           /* 2560 (4B) or 2048 (1.7B); a multiple of 8     */
+  float rms_eps;            /* the RMSNorm epsilon, > 0                      */
+} hattn_block_weights;
+
+/* Prefill of the block over a ragged batch, layouts as hattn_prefill_varlen:
+ *   x:   bf16 [T][hidden] block inputs of the packed new tokens
+ *   out: bf16 [T][hidden]; may be x (the residual stream updated in place)
+ * The rotated keys and the values go to the cache as in hattn_prefill.
+ * Errors: as hattn_prefill_varlen, plus HATTN_ERR_SHAPE for a hidden size
+ * that is not a positive multiple of 8 or rms_eps <= 0, HATTN_ERR_NULL for
+ * a missing weight, and HATTN_ERR_LAUNCH when hipBLASLt fails. */
+size_t hattn_block_prefill_workspace_size(const hattn_layer_desc* desc,
+                                          const hattn_block_weights* w,
+                                          const hattn_kv_cache* cache,
+                                          int32_t batch,
+                                          const int32_t* cu_seqlens);
+int hattn_block_prefill(const hattn_layer_desc* desc,
+                        const hattn_block_weights* w, const void* x,
+                        int32_t batch, const int32_t* cu_seqlens,
+                        const int32_t* start_pos, const hattn_kv_cache* cache,
+                        void* out, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/* Decode of the block: x, out bf16 [B][hidden] (out may be x); pos,
+ * max_pos and the cache as in hattn_decode. Errors as hattn_decode plus
+ * those of hattn_block_prefill's weights. */
+size_t hattn_block_decode_workspace_size(const hattn_layer_desc* desc,
+                                         const hattn_block_weights* w,
+                                         const hattn_kv_cache* cache,
+                                         int32_t batch);
+int hattn_block_decode(const hattn_layer_desc* desc,
+                       const hattn_block_weights* w, const void* x,
+                       int32_t batch, const int32_t* pos, int32_t max_pos,
+                       const hattn_kv_cache* cache, void* out,
+                       void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * KV planner (page §6 参数与 KV Cache 估算, KV table: K and V of every KV

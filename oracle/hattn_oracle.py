@@ -381,6 +381,71 @@ def decode_ref(q, k, v, gate, pos, cache_k, cache_v, *, kind, window, theta,
     return out, slots, k_hats
 
 
+# --------------------------------------------------------------------------
+# the attention block around the core  [SPARK §2 figure 1 (decoder-layer
+# dataflow), §1 config table, §3, §5]
+# --------------------------------------------------------------------------
+def rms_norm(x, weight, eps):
+    """[SPARK §5] RMSNorm: computed in higher precision (fp64 here; the page
+    says the model upcasts to fp32), multiplied by the weight, then cast
+    back to the model dtype (bf16, one rounding)."""
+    x = f64(x)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    return bf16_rne(x * r * f64(weight))
+
+
+def linear_bf16(x, w):
+    """A bias-free Linear of the model ([SPARK §5]: attention_bias false):
+    x [..., in] @ w[out, in]^T in fp64, output cast to bf16."""
+    return bf16_rne(f64(x) @ f64(w).T)
+
+
+def split_qkvg(y, Hq, Hkv, D=HEAD_DIM):
+    """The fused projection's output [T, Hq*D + 2*Hkv*D + Hq] split into
+    q [T, Hq, D], k and v [T, Hkv, D] (q_k_v_proj, [SPARK §3]: 4096 + 2 x
+    1024 outputs on the 4B shape, read as Q then K then V) and the gate
+    logits [T, Hq] (g_proj, one per head)."""
+    T = y.shape[0]
+    q = y[:, :Hq * D].reshape(T, Hq, D)
+    k = y[:, Hq * D:(Hq + Hkv) * D].reshape(T, Hkv, D)
+    v = y[:, (Hq + Hkv) * D:(Hq + 2 * Hkv) * D].reshape(T, Hkv, D)
+    g = y[:, (Hq + 2 * Hkv) * D:]
+    if g.shape[1] != Hq:
+        raise ValueError("fused projection width does not match the head counts")
+    return q, k, v, g
+
+
+def block_prefill_ref(x, norm_w, w_qkvg, w_o, eps, cu_seqlens, start_pos, *, Hq, Hkv,
+                      window, theta, rotary_fraction, gate_act="sigmoid", hist_k=None,
+                      hist_v=None, hist_pos=None):
+    """One attention block over a ragged batch of new tokens x [T, hidden]
+    ([SPARK] figure 1): RMSNorm -> fused q/k/v/g projection -> the core
+    (prefill_varlen_ref) -> out_proj -> + residual. Tensors between modules
+    are bf16 (the model dtype; the core's output is cast back as [SPARK §3]
+    states); the returned sum x + out_proj(...) is left unrounded.
+    Returns (out [T, hidden] fp64, k_hat [T, Hkv, D])."""
+    h = rms_norm(x, norm_w, eps)
+    q, k, v, g = split_qkvg(linear_bf16(h, w_qkvg), Hq, Hkv)
+    attn, k_hat = prefill_varlen_ref(q, k, v, g, cu_seqlens, start_pos, window=window, theta=theta,
+                                     rotary_fraction=rotary_fraction, hist_k=hist_k, hist_v=hist_v,
+                                     hist_pos=hist_pos, gate_act=gate_act)
+    y = linear_bf16(bf16_rne(attn).reshape(attn.shape[0], -1), w_o)
+    return f64(x) + y, k_hat
+
+
+def block_decode_ref(x, norm_w, w_qkvg, w_o, eps, pos, cache_k, cache_v, *, Hq, Hkv, kind,
+                     window, theta, rotary_fraction, gate_act="sigmoid"):
+    """The block for one new token per sequence, x [B, hidden], over the
+    caches as decode_ref reads them. Returns (out [B, hidden] fp64 unrounded,
+    slots, k_hat)."""
+    h = rms_norm(x, norm_w, eps)
+    q, k, v, g = split_qkvg(linear_bf16(h, w_qkvg), Hq, Hkv)
+    attn, slots, k_hat = decode_ref(q, k, v, g, pos, cache_k, cache_v, kind=kind, window=window,
+                                    theta=theta, rotary_fraction=rotary_fraction, gate_act=gate_act)
+    y = linear_bf16(bf16_rne(attn).reshape(attn.shape[0], -1), w_o)
+    return f64(x) + y, slots, k_hat
+
+
 def paged_to_linear(pool, table, page_size):
     """The linear view [B, Hkv, pages_per_seq * page_size, D] of a paged
     cache: pool [num_pages, Hkv, page_size, D], table [B, pages_per_seq];

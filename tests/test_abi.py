@@ -158,6 +158,37 @@ def test_prefill_varlen_rejects_bad_arguments(L):
     assert got == 400 * 128 * 8 + 2 * 3 * 4 * (511 + 270) * 256 * 2
 
 
+def test_block_rejects_bad_arguments(L):
+    fu = hb.layer_desc("full")
+    lin = hb.KvCacheC(FAKE, FAKE, hb.KV_LINEAR, 2, 4096)
+    cu = (ctypes.c_int32 * 3)(0, 100, 130)
+    sp = (ctypes.c_int32 * 2)(0, 0)
+    def pre(w, x=FAKE, out=FAKE, ws_bytes=1 << 34):
+        return L.hattn_block_prefill(ctypes.byref(fu), ctypes.byref(w) if w is not None else None, x, 2,
+                                     ctypes.cast(cu, ctypes.c_void_p), ctypes.cast(sp, ctypes.c_void_p),
+                                     ctypes.byref(lin), out, FAKE, ws_bytes, None)
+    good = hb.BlockWeightsC(FAKE, FAKE, FAKE, 2560, 1e-6)
+    assert pre(None) == -1
+    assert pre(hb.BlockWeightsC(0, FAKE, FAKE, 2560, 1e-6)) == -1
+    assert pre(hb.BlockWeightsC(FAKE, FAKE, FAKE, 2561, 1e-6)) == -2      # hidden not a multiple of 8
+    assert pre(hb.BlockWeightsC(FAKE, FAKE, FAKE, 2560, 0.0)) == -2       # eps must be positive
+    assert pre(hb.BlockWeightsC(FAKE, FAKE + 8, FAKE, 2560, 1e-6)) == -9
+    assert pre(good, x=0) == -1
+    assert pre(good, x=FAKE + 2) == -9
+    assert pre(good, ws_bytes=1024) == -8
+    # workspace: h, the fused projection, the core's output, out_proj's
+    # output, 32 MiB of GEMM workspace, then the core's own (cos/sin table)
+    T, H, n1 = 130, 2560, (16 + 8) * 256 + 16
+    a = lambda b: (b + 255) // 256 * 256
+    want = a(T * H * 2) + a(T * n1 * 2) + a(T * 4096 * 2) + a(T * H * 2) + (32 << 20) + a(T * 32 * 8)
+    got = L.hattn_block_prefill_workspace_size(ctypes.byref(fu), ctypes.byref(good), ctypes.byref(lin), 2,
+                                               ctypes.cast(cu, ctypes.c_void_p))
+    assert got == want
+    dec = L.hattn_block_decode(ctypes.byref(fu), ctypes.byref(hb.BlockWeightsC(FAKE, FAKE, FAKE, 0, 1e-6)), FAKE, 2,
+                               FAKE, 10, ctypes.byref(lin), FAKE, FAKE, 1 << 34, None)
+    assert dec == -2
+
+
 def test_decode_rejects_bad_arguments(L):
     sl = hb.layer_desc("sliding")
     fu = hb.layer_desc("full")

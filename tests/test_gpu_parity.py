@@ -561,6 +561,99 @@ def test_paged_chunked_prefill_equals_linear_prefill():
     check("paged chunked prefill", o_pg.cpu(), ref)
 
 
+def check_block(tag, gpu, ref, x):
+    """The block's output is x + y with y = out_proj(...) itself a bf16
+    module output: an upstream difference of any size can move y's rounding
+    by one bf16 ulp, and the store rounds the sum once more. Each element's
+    max-abs bar is widened by one ulp of y (y = ref - x exactly, both being
+    bf16 values) on top of the store allowance; the relative RMS bar is
+    unchanged."""
+    assert torch.isfinite(gpu.float()).all(), f"{tag}: non-finite output"
+    g = O.f64(gpu.float().cpu())
+    y = ref - O.f64(x)
+    ay = np.abs(y)
+    ulp_y = np.where(ay > 0, 2.0 ** (np.floor(np.log2(np.maximum(ay, 2.0 ** -126))) - 7), 0.0)
+    d = np.abs(g - ref)
+    eq = float((d - store_allowance(ref) - ulp_y).max())
+    er = float(np.linalg.norm(g - ref) / np.linalg.norm(ref))
+    log(f"[parity] {tag}: max_abs={d.max():.3e} (beyond the roundings of y and of the store {eq:.3e}) "
+        f"rel_rms={er:.3e} max|ref|={np.abs(ref).max():.3f} max|y|={ay.max():.3f}")
+    assert eq <= MAX_ABS and er <= REL_RMS, (tag, d.max(), eq, er)
+
+
+def _block(hidden, Hq, Hkv, seed):
+    w = synth.block_weights(hidden, Hq, Hkv, seed=seed)
+    dev = hb.BlockWeights(w["norm"].to(DEV), w["qkvg"].to(DEV), w["o"].to(DEV), rms_eps=1e-6)
+    return w, dev
+
+
+@pytest.mark.parametrize("layer,hidden,Hq,Hkv,kind,cap", [
+    ("full", 2560, 16, 4, "linear", 2048),     # the 4B shape
+    ("sliding", 2048, 8, 2, "ring", 512),      # the 1.7B shape
+])
+def test_block_prefill_and_decode(layer, hidden, Hq, Hkv, kind, cap):
+    # RMSNorm -> fused q/k/v/g projection -> core -> out_proj -> + residual,
+    # on a ragged batch over cached histories, then one decode step
+    desc = hb.layer_desc(layer, Hq, Hkv)
+    w, wd = _block(hidden, Hq, Hkv, seed=120)
+    lens, starts = [300, 77, 1], [0, 1000, 5]
+    B, T = len(lens), sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    x = synth.hidden_states(T, hidden, seed=121)
+    ck = synth.cache_tensor(B, Hkv, cap, seed=122)
+    cv = synth.cache_tensor(B, Hkv, cap, seed=123)
+    cache = hb.KVCache(ck.to(DEV), cv.to(DEV), kind)
+    out = hb.hattn_block_prefill(desc, wd, x.to(DEV), cu, starts, cache)
+    torch.cuda.synchronize()
+    hk, hv, hp = history_for(kind, ck, cv, starts, cap)
+    win = desc.window if desc.window > 0 else None
+    kw = dict(Hq=Hq, Hkv=Hkv, window=win, theta=desc.rope_theta, rotary_fraction=desc.rotary_fraction)
+    ref, k_hat = O.block_prefill_ref(x, w["norm"], w["qkvg"], w["o"], 1e-6, cu, starts, hist_k=hk, hist_v=hv,
+                                     hist_pos=hp, **kw)
+    check_block(f"block prefill {layer} hidden={hidden}", out.cpu(), ref, x)
+    # in place (out is x) gives the same bits
+    cache2 = hb.KVCache(ck.to(DEV), cv.to(DEV), kind)
+    xi = x.to(DEV)
+    hb.hattn_block_prefill(desc, wd, xi, cu, starts, cache2, out=xi)
+    torch.cuda.synchronize()
+    assert torch.equal(xi, out)
+    # decode of the next token of every sequence on the updated cache
+    hk2, hv2 = cache_after_varlen_prefill(ck, cv, k_hat, _v_of_block(x, w, Hq, Hkv), cu, starts, kind, cap)
+    xd = synth.hidden_states(B, hidden, seed=124)
+    pos = np.array([s + n for s, n in zip(starts, lens)])
+    od = hb.hattn_block_decode(desc, wd, xd.to(DEV), torch.as_tensor(pos, dtype=torch.int32).to(DEV),
+                               int(pos.max()), cache)
+    torch.cuda.synchronize()
+    kd = dict(kw)
+    kd.pop("window")
+    ref_d, _, _ = O.block_decode_ref(xd, w["norm"], w["qkvg"], w["o"], 1e-6, pos, hk2, hv2, kind=kind, window=win,
+                                     **kd)
+    check_block(f"block decode {layer} hidden={hidden}", od.cpu(), ref_d, xd)
+
+
+def cache_after_varlen_prefill(ck, cv, k_hat, v, cu, start, kind, cap):
+    """cache_after_prefill for packed new tokens (sequence b: rows cu[b] ..
+    cu[b+1]-1 of k_hat and v)."""
+    hk, hv = O.f64(ck).copy(), O.f64(cv).copy()
+    vv = O.f64(v)
+    for b in range(len(cu) - 1):
+        S = cu[b + 1] - cu[b]
+        keep = min(S, cap) if kind == "ring" else S
+        for i in range(S - keep, S):
+            p = start[b] + i
+            slot = p % cap if kind == "ring" else p
+            hk[b, :, slot] = k_hat[cu[b] + i]
+            hv[b, :, slot] = vv[cu[b] + i]
+    return hk, hv
+
+
+def _v_of_block(x, w, Hq, Hkv):
+    """The values the block's projection gives for inputs x (the oracle's
+    own arithmetic), [T, Hkv, 256]."""
+    h = O.rms_norm(x, w["norm"], 1e-6)
+    return O.split_qkvg(O.linear_bf16(h, w["qkvg"]), Hq, Hkv)[2]
+
+
 def test_ring_decode_equals_windowed_linear_decode():
     B, p = 4, 3000
     desc = hb.layer_desc("sliding")

@@ -418,3 +418,77 @@ def test_kv_sizing_matches_page_table():
     ratio = O.kv_bytes_model(36, 4, T) / O.kv_bytes_model(36, 4, T, hybrid=False)
     assert abs(ratio - t["ratio_hybrid_over_all_full"]) <= t["ratio_rel_tol"]
     assert O.kv_bytes_model(36, 4, 1 << 20, hybrid=False) == t["all_full_2pow20_GiB_explainer_page"] * 2 ** 30
+
+
+# ----------------------------------------------------------------- the attention block
+def _block_case(T=9, H=64, Hq=4, Hkv=1, seed=31):
+    rng = np.random.default_rng(seed)
+    D = 256
+    x = O.bf16_rne(rng.standard_normal((T, H)))
+    nw = O.bf16_rne(1.0 + 0.1 * rng.standard_normal(H))
+    wq = O.bf16_rne(0.05 * rng.standard_normal(((Hq + 2 * Hkv) * D + Hq, H)))
+    wo = O.bf16_rne(0.02 * rng.standard_normal((H, Hq * D)))
+    return x, nw, wq, wo
+
+
+def test_rms_norm_against_torch_and_closed_form():
+    rng = np.random.default_rng(32)
+    x = O.bf16_rne(rng.standard_normal((7, 96)))
+    w = O.bf16_rne(1.0 + 0.1 * rng.standard_normal(96))
+    got = O.rms_norm(x, w, 1e-6)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (96,), torch.from_numpy(w), 1e-6).numpy()
+    # one bf16 rounding of the library's fp64 result: within half an ulp of it
+    half_ulp = 2.0 ** (np.floor(np.log2(np.abs(ref))) - 8)
+    assert np.all(np.abs(got - ref) <= half_ulp * (1 + 1e-12))
+    # a constant row c: every channel becomes w * c / sqrt(c^2 + eps)
+    c, eps = -1.5, 1e-6
+    got = O.rms_norm(np.full((1, 96), c), w, eps)
+    assert np.array_equal(got[0], O.bf16_rne(w * c / math.sqrt(c * c + eps)))
+
+
+def test_block_with_zero_out_proj_returns_the_residual():
+    x, nw, wq, _ = _block_case()
+    wo = np.zeros((x.shape[1], 4 * 256))
+    out, _ = O.block_prefill_ref(x, nw, wq, wo, 1e-6, [0, x.shape[0]], [0], Hq=4, Hkv=1, window=None,
+                                 theta=5e6, rotary_fraction=0.25)
+    assert np.array_equal(out, x)
+
+
+def test_block_projection_orientation_and_split_order():
+    # out_proj as a permutation matrix: y[:, i] = attn[:, sigma(i)]; the
+    # fused projection rows pick normed channels, so q/k/v/g are known slices
+    T, H, Hq, Hkv, D = 6, 4 * 256, 4, 1, 256
+    rng = np.random.default_rng(33)
+    x = O.bf16_rne(rng.standard_normal((T, H)))
+    nw = np.ones(H)
+    tau = rng.integers(0, H, (Hq + 2 * Hkv) * D + Hq)
+    wq = np.zeros((tau.size, H))
+    wq[np.arange(tau.size), tau] = 1.0
+    sigma = rng.permutation(Hq * D)
+    wo = np.zeros((H, Hq * D))
+    wo[np.arange(H), sigma] = 1.0
+    kw = dict(window=None, theta=5e6, rotary_fraction=0.25)
+    out, _ = O.block_prefill_ref(x, nw, wq, wo, 1e-6, [0, T], [3], Hq=Hq, Hkv=Hkv, **kw)
+    h = O.rms_norm(x, nw, 1e-6)[:, tau]
+    q = h[:, :Hq * D].reshape(T, Hq, D)
+    k = h[:, Hq * D:(Hq + 1) * D].reshape(T, 1, D)
+    v = h[:, (Hq + 1) * D:(Hq + 2) * D].reshape(T, 1, D)
+    g = h[:, (Hq + 2) * D:]
+    attn, _ = O.prefill_varlen_ref(q, k, v, g, [0, T], [3], **kw)
+    assert np.array_equal(out, x + O.bf16_rne(attn).reshape(T, -1)[:, sigma])
+
+
+def test_block_decode_equals_block_prefill_row():
+    x, nw, wq, wo = _block_case(T=9)
+    kw = dict(Hq=4, Hkv=1, window=None, theta=5e6, rotary_fraction=0.25, gate_act="sigmoid")
+    full, k_hat = O.block_prefill_ref(x, nw, wq, wo, 1e-6, [0, 9], [0], **kw)
+    h = O.rms_norm(x[:8], nw, 1e-6)
+    _, _, v8, _ = O.split_qkvg(O.linear_bf16(h, wq), 4, 1)
+    ck = np.zeros((1, 1, 16, 256))
+    cv = np.zeros((1, 1, 16, 256))
+    ck[0, 0, :8] = k_hat[:8, 0]
+    cv[0, 0, :8] = v8[:, 0]
+    kd = dict(kw)
+    kd.pop("window")
+    dec, _, _ = O.block_decode_ref(x[8:9], nw, wq, wo, 1e-6, [8], ck, cv, kind="linear", window=None, **kd)
+    np.testing.assert_allclose(dec[0], full[8], rtol=0, atol=1e-12)
