@@ -654,6 +654,58 @@ def _v_of_block(x, w, Hq, Hkv):
     return O.split_qkvg(O.linear_bf16(h, w["qkvg"]), Hq, Hkv)[2]
 
 
+def test_decode_and_prefill_replay_from_a_captured_hip_graph():
+    # serving loops capture the call once and replay it with new positions in
+    # device memory: every replay must equal the eager call on the same state
+    B = 16
+    desc = hb.layer_desc("sliding")
+    inp = to_dev(synth.decode_inputs(B, 16, 4, seed=130))
+    ck = synth.cache_tensor(B, 4, 512, seed=131).to(DEV)
+    cv = synth.cache_tensor(B, 4, 512, seed=132).to(DEV)
+    g_cache = hb.KVCache(ck.clone(), cv.clone(), "ring")
+    pos = torch.zeros(B, dtype=torch.int32, device=DEV)
+    out = torch.empty_like(inp["q"])
+    ws = torch.empty(max(hb.decode_workspace_size(desc, g_cache, B), 256), dtype=torch.uint8, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm the library's one-time work outside the capture
+        hb.hattn_decode(desc, inp["q"], inp["k"], inp["v"], inp["gate"], pos, 1 << 20, g_cache, out=out,
+                        workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        hb.hattn_decode(desc, inp["q"], inp["k"], inp["v"], inp["gate"], pos, 1 << 20, g_cache, out=out,
+                        workspace=ws)
+    e_cache = hb.KVCache(g_cache.k.clone(), g_cache.v.clone(), "ring")
+    for step, p0 in enumerate([600, 601, 5000, 123456]):
+        newpos = torch.arange(B, dtype=torch.int32) * 7 + p0
+        pos.copy_(newpos.to(DEV))
+        graph.replay()
+        torch.cuda.synchronize()
+        e_out = hb.hattn_decode(desc, inp["q"], inp["k"], inp["v"], inp["gate"], newpos.to(DEV), 1 << 20, e_cache)
+        torch.cuda.synchronize()
+        assert torch.equal(out, e_out), step
+        assert torch.equal(g_cache.k, e_cache.k) and torch.equal(g_cache.v, e_cache.v), step
+    # a prefill call captured and replayed twice over the same inputs
+    pdesc = hb.layer_desc("full")
+    pin = to_dev(synth.prefill_inputs(1, 300, 16, 4, seed=133))
+    pc = hb.KVCache.empty(1, 4, 512, "linear")
+    pout = torch.empty_like(pin["q"])
+    pws = torch.empty(max(hb.prefill_workspace_size(pdesc, pc, 1, 300), 256), dtype=torch.uint8, device=DEV)
+    hb.hattn_prefill(pdesc, pin["q"], pin["k"], pin["v"], pin["gate"], [0], pc, out=pout, workspace=pws)
+    torch.cuda.synchronize()
+    eager = pout.clone()
+    pgraph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(pgraph):
+        hb.hattn_prefill(pdesc, pin["q"], pin["k"], pin["v"], pin["gate"], [0], pc, out=pout, workspace=pws)
+    for _ in range(2):
+        pout.zero_()
+        pgraph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(pout, eager)
+
+
 def test_ring_decode_equals_windowed_linear_decode():
     B, p = 4, 3000
     desc = hb.layer_desc("sliding")
