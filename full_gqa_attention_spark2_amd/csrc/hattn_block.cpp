@@ -5,6 +5,7 @@
 // this library's kernels.
 #include <stdint.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -20,6 +21,7 @@ namespace {
 
 constexpr size_t kGemmWorkspace = 32u << 20;  // hipBLASLt workspace per GEMM
 constexpr int kGemmCandidates = 16;           // heuristic results considered
+constexpr int kTunedCandidates = 8;           // of those, timed on the first call of a shape
 constexpr int kMaxDevices = 64;
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -41,12 +43,15 @@ hipblasLtHandle_t lt_handle() {
 struct GemmPlan {
   hipblasLtMatmulDesc_t op = nullptr;
   hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, ld = nullptr;
-  hipblasLtMatmulAlgo_t algo{};
+  hipblasLtMatmulAlgo_t algo{};                       // the one in use
+  hipblasLtMatmulAlgo_t cand[kGemmCandidates]{};      // heuristic candidates that fit the workspace
+  int n_cand = 0;
+  bool tuned = false;  // algo is the fastest candidate measured on this shape
   bool ok = false;
 };
 std::map<std::tuple<int, int, int, long long, long long, int>, GemmPlan> g_plans;
 
-const GemmPlan* gemm_plan(hipblasLtHandle_t h, int N, int K, int T, long long lda, long long ldd) {
+GemmPlan* gemm_plan(hipblasLtHandle_t h, int N, int K, int T, long long lda, long long ldd) {
   int dev = 0;
   (void)hipGetDevice(&dev);
   std::lock_guard<std::mutex> lock(g_mu);
@@ -73,15 +78,53 @@ const GemmPlan* gemm_plan(hipblasLtHandle_t h, int N, int K, int T, long long ld
     int n = 0;
     ok = ok && hipblasLtMatmulAlgoGetHeuristic(h, p.op, p.la, p.lb, p.ld, p.ld, pref, kGemmCandidates, res, &n) ==
                    HIPBLAS_STATUS_SUCCESS;
-    int pick = -1;
-    for (int i = 0; ok && i < n && pick < 0; ++i)
-      if (res[i].state == HIPBLAS_STATUS_SUCCESS && res[i].workspaceSize <= kGemmWorkspace) pick = i;
-    ok = ok && pick >= 0;
-    if (ok) p.algo = res[pick].algo;
+    for (int i = 0; ok && i < n; ++i)
+      if (res[i].state == HIPBLAS_STATUS_SUCCESS && res[i].workspaceSize <= kGemmWorkspace)
+        p.cand[p.n_cand++] = res[i].algo;
+    ok = ok && p.n_cand > 0;
+    if (ok) p.algo = p.cand[0];
     if (pref) hipblasLtMatmulPreferenceDestroy(pref);
   }
   p.ok = ok;
   return (g_plans[key] = p).ok ? &g_plans[key] : nullptr;
+}
+
+// The first call of a shape outside stream capture times the first
+// kTunedCandidates candidates on its own buffers (twice each, best of two)
+// and keeps the fastest; the heuristic's ranking is often not the fastest
+// order on this chip. Under capture the top candidate is used untimed.
+void tune(hipblasLtHandle_t h, GemmPlan* p, const void* W, const void* A, void* D, void* ws, hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (p->tuned || p->n_cand < 2 || hipStreamIsCapturing(s, &cs) != hipSuccess ||
+      cs != hipStreamCaptureStatusNone)
+    return;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return;
+  }
+  const float alpha = 1.f, beta = 0.f;
+  float best = 1e30f;
+  for (int i = 0; i < p->n_cand && i < kTunedCandidates; ++i) {
+    float t_i = 1e30f;
+    for (int r = 0; r < 2; ++r) {
+      float ms = 0.f;
+      if (hipEventRecord(e0, s) != hipSuccess ||
+          hipblasLtMatmul(h, p->op, &alpha, W, p->la, A, p->lb, &beta, D, p->ld, D, p->ld, &p->cand[i], ws,
+                          kGemmWorkspace, s) != HIPBLAS_STATUS_SUCCESS ||
+          hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+          hipEventElapsedTime(&ms, e0, e1) != hipSuccess)
+        break;
+      t_i = std::min(t_i, ms);
+    }
+    if (t_i < best) {
+      best = t_i;
+      p->algo = p->cand[i];
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  p->tuned = true;
 }
 
 int gemm(const void* W, int N, int K, const void* A, int T, long long lda, void* D, long long ldd, void* ws,
@@ -89,8 +132,12 @@ int gemm(const void* W, int N, int K, const void* A, int T, long long lda, void*
   if (T == 0) return HATTN_OK;
   hipblasLtHandle_t h = lt_handle();
   if (!h) return HATTN_ERR_LAUNCH;
-  const GemmPlan* p = gemm_plan(h, N, K, T, lda, ldd);
+  GemmPlan* p = gemm_plan(h, N, K, T, lda, ldd);
   if (!p) return HATTN_ERR_LAUNCH;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    tune(h, p, W, A, D, ws, s);
+  }
   const float alpha = 1.f, beta = 0.f;
   return hipblasLtMatmul(h, p->op, &alpha, W, p->la, A, p->lb, &beta, D, p->ld, D, p->ld, &p->algo, ws,
                          kGemmWorkspace, s) == HIPBLAS_STATUS_SUCCESS
