@@ -310,6 +310,9 @@ int prefill_packed(const hattn_layer_desc* desc, const void* q, const void* k, c
   // (A paged cache is addressed per page.)
   const long long key_rows = ring ? (long long)desc->window - 1 + max_len : (long long)cache->capacity;
   if (cache->kind != HATTN_KV_PAGED && key_rows > kMaxPrefillKeyRows) return HATTN_ERR_UNSUPPORTED;
+  // one-dimensional grids: (query blocks x sequences x KV heads) workgroups
+  if ((long long)((max_len + kPrefillBlockQ - 1) / kPrefillBlockQ) * batch * desc->num_kv_heads > INT32_MAX)
+    return HATTN_ERR_UNSUPPORTED;
   const PrefillLayout L = prefill_layout(desc, cache, batch, total, max_len);
   if (!workspace || workspace_bytes < L.total) return HATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return HATTN_ERR_ALIGN;
@@ -503,6 +506,9 @@ int decode_strided(const hattn_layer_desc* desc, const void* q, const void* k, c
   if (cache->kind != HATTN_KV_RING && max_pos >= cache->capacity) return HATTN_ERR_CAPACITY;
   const long long span = decode_span(desc, cache, max_pos);
   const DecodePlan p = decode_plan(desc, cache, batch, span);
+  // one-dimensional grids: (sequences x KV heads x splits) and (sequences x heads)
+  if ((long long)batch * desc->num_kv_heads * p.nsplit > INT32_MAX || (long long)batch * desc->num_q_heads > INT32_MAX)
+    return HATTN_ERR_UNSUPPORTED;
   const size_t parts = (size_t)batch * desc->num_q_heads * p.nsplit;
   const size_t o_bytes = align_up(parts * desc->head_dim * 4, 256);
   const size_t need = p.nsplit == 1 ? 0 : o_bytes + align_up(parts * 2 * 4, 256);
