@@ -127,6 +127,59 @@ def test_rope_apply_matches_oracle(layer):
     torch.cuda.synchronize()
     check_bf16_values(f"rope_apply {layer}", xd, ref)
     assert torch.equal(xd[0].cpu(), x[0])  # position 0 is the identity
+    r = int(256 * prm["rotary_fraction"])
+    assert torch.equal(xd[:, :, r:].cpu(), x[:, :, r:])  # channels past r pass through
+
+
+def test_gpu_gate_and_window_invariants():
+    # the gate: out(g = 0) is exactly half of out(g = +30) (sigmoid(30) is
+    # 1.0 in fp32, and halving commutes with the bf16 store)
+    desc = hb.layer_desc("full")
+    inp = synth.prefill_inputs(1, 200, 16, 4, seed=140)
+    outs = []
+    for gv in (0.0, 30.0):
+        d = to_dev(inp)
+        d["gate"] = torch.full_like(d["gate"], gv)
+        cache = hb.KVCache.empty(1, 4, 256, "linear")
+        outs.append(hb.hattn_prefill(desc, d["q"], d["k"], d["v"], d["gate"], [0], cache))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], (outs[1].float() * 0.5).to(torch.bfloat16))
+    # a window covering every query-key distance gives exactly the causal result
+    S = 300
+    inp = to_dev(synth.prefill_inputs(1, S, 16, 4, seed=141))
+    full = hb.layer_desc("full")
+    wide = hb.layer_desc("sliding", rope_theta=full.rope_theta, rotary_fraction=full.rotary_fraction, window=S + 7)
+    c1 = hb.KVCache.empty(1, 4, S, "linear")
+    c2 = hb.KVCache.empty(1, 4, S, "linear")
+    o1 = hb.hattn_prefill(full, inp["q"], inp["k"], inp["v"], inp["gate"], [0], c1)
+    o2 = hb.hattn_prefill(wide, inp["q"], inp["k"], inp["v"], inp["gate"], [0], c2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_decode_split_count_does_not_change_the_result():
+    # the same four sequences decoded alone (a split plan: several
+    # workgroups per sequence, merged) and inside a batch of 64 (one
+    # workgroup per sequence): equal up to the order of the sums
+    desc = hb.layer_desc("sliding")
+    pos = synth.positions_uniform(64, 512, 1 << 20, seed=142).numpy()
+    inp = synth.decode_inputs(64, 16, 4, seed=143)
+    ck = synth.cache_tensor(64, 4, 512, seed=144)
+    cv = synth.cache_tensor(64, 4, 512, seed=145)
+    big = hb.KVCache(ck.to(DEV), cv.to(DEV), "ring")
+    d = to_dev(inp)
+    o64 = hb.hattn_decode(desc, d["q"], d["k"], d["v"], d["gate"], torch.as_tensor(pos).to(DEV), int(pos.max()), big)
+    small = hb.KVCache(ck[:4].to(DEV), cv[:4].to(DEV), "ring")
+    s4 = {k: v[:4].contiguous() for k, v in d.items()}
+    o4 = hb.hattn_decode(desc, s4["q"], s4["k"], s4["v"], s4["gate"], torch.as_tensor(pos[:4]).to(DEV),
+                         int(pos[:4].max()), small)
+    torch.cuda.synchronize()
+    diff = (o4.float() - o64[:4].float()).abs()
+    rel = (diff.norm() / o64[:4].float().norm()).item()
+    log(f"[parity] split vs wide decode: max diff {diff.max().item():.3e}, relative RMS {rel:.3e}")
+    # a tenth of the parity bars: only the order of fp32 sums differs
+    assert diff.max().item() <= MAX_ABS / 10 and rel <= REL_RMS / 10
+    assert torch.equal(small.k, big.k[:4]) and torch.equal(small.v, big.v[:4])
 
 
 # ------------------------------------------------------------------ prefill
