@@ -684,6 +684,24 @@ def test_block_prefill_and_decode(layer, hidden, Hq, Hkv, kind, cap):
     check_block(f"block decode {layer} hidden={hidden}", od.cpu(), ref_d, xd)
 
 
+@pytest.mark.parametrize("B", [17, 64])
+def test_block_decode_token_counts(B):
+    # decode batches of 17 and 64 sequences: the weight-streaming GEMM's
+    # partial and full token blocks
+    desc = hb.layer_desc("sliding")
+    w, wd = _block(2560, 16, 4, seed=150)
+    ck = synth.cache_tensor(B, 4, 512, seed=151)
+    cv = synth.cache_tensor(B, 4, 512, seed=152)
+    cache = hb.KVCache(ck.to(DEV), cv.to(DEV), "ring")
+    pos = synth.positions_uniform(B, 0, 1 << 20, seed=153).numpy()
+    x = synth.hidden_states(B, 2560, seed=154)
+    out = hb.hattn_block_decode(desc, wd, x.to(DEV), torch.as_tensor(pos).to(DEV), int(pos.max()), cache)
+    torch.cuda.synchronize()
+    ref, _, _ = O.block_decode_ref(x, w["norm"], w["qkvg"], w["o"], 1e-6, pos, ck, cv, Hq=16, Hkv=4, kind="ring",
+                                   window=512, theta=desc.rope_theta, rotary_fraction=desc.rotary_fraction)
+    check_block(f"block decode B={B}", out.cpu(), ref, x)
+
+
 def cache_after_varlen_prefill(ck, cv, k_hat, v, cu, start, kind, cap):
     """cache_after_prefill for packed new tokens (sequence b: rows cu[b] ..
     cu[b+1]-1 of k_hat and v)."""
