@@ -152,10 +152,12 @@ size_t hattn_prefill_workspace_size(const hattn_layer_desc* desc,
  *   out:  bf16 [B][S][num_q_heads][256]; must not alias any input.
  * Cache slots outside the history may hold any bits, NaN included; they
  * never reach the result. The rotated keys and the values of the new tokens
- * are written to the cache (a ring keeps the last min(S, capacity) of them). B <= 128, and the key
- * rows of one (sequence, KV head) -- a linear cache's capacity, or
- * window - 1 + S for a ring -- must not exceed 2^23; larger calls return
- * HATTN_ERR_UNSUPPORTED. */
+ * are written to the cache (a ring keeps the last min(S, capacity) of
+ * them). Limits, beyond which a call returns HATTN_ERR_UNSUPPORTED: B <=
+ * 128; the key rows of one (sequence, KV head) -- a linear cache's
+ * capacity, or window - 1 + S for a ring; paged caches are addressed page
+ * by page and exempt -- at most 2^23; ceil(S / 32) * B * num_kv_heads
+ * below 2^31. */
 int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k,
                   const void* v, const void* gate, int32_t batch,
                   int32_t seq_len, const int32_t* start_pos,
@@ -197,13 +199,15 @@ size_t hattn_decode_workspace_size(const hattn_layer_desc* desc,
  *   q:    bf16 [B][num_q_heads][256], k, v: bf16 [B][num_kv_heads][256]
  *   gate: bf16 [B][num_q_heads]
  *   pos:  int32 [B], DEVICE memory; max_pos: a host upper bound of pos[]
- *     (checked against a linear cache's capacity).
+ *     (checked against a linear or paged cache's capacity).
  *   out:  bf16 [B][num_q_heads][256]
  * The cache must hold positions 0 .. pos[b]-1 (slots outside the visible
  * range may hold any bits, NaN included; they never reach the result). The
  * new rotated key and value are written to their slot, and the attention
  * includes them. A pos[b] outside [0, max_pos] yields a NaN output row and
- * no cache write. */
+ * no cache write. The call holds no host synchronisation and reads the
+ * positions on the device, so it can be captured in a HIP graph and
+ * replayed with new positions. */
 int hattn_decode(const hattn_layer_desc* desc, const void* q, const void* k,
                  const void* v, const void* gate, int32_t batch,
                  const int32_t* pos, int32_t max_pos,
@@ -221,6 +225,9 @@ int hattn_decode(const hattn_layer_desc* desc, const void* q, const void* k,
  * Linear layers have no bias (page §5: attention_bias false). The GEMMs run
  * on hipBLASLt (bf16 in and out, fp32 accumulate) through one handle per
  * device, created on first use; the other steps are this library's kernels.
+ * The first call of a GEMM shape outside stream capture times a few
+ * hipBLASLt candidates on its own buffers and waits for them (once per
+ * shape and process); later calls, and calls under capture, do not wait.
  */
 typedef struct {
   const void* norm_weight;  /* bf16 [hidden]: the input RMSNorm's weight    */
