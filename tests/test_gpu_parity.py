@@ -1042,3 +1042,40 @@ def test_seeded_sweep_of_small_configurations(seed):
         for b in range(B):
             check_bf16_values(f"{tag} paged key b={b}", lk[b, :, int(slots[b])], k_hat_d[b])
             assert torch.equal(lv[b, :, int(slots[b])], dinp["v"][b])
+
+
+def test_largest_positions_and_batch():
+    # positions at the top of the documented range (just below 2^30), where
+    # the RoPE angle reaches ~1e9 rad, and the largest prefill batch (128)
+    top = (1 << 30) - 1
+    desc = hb.layer_desc("sliding")
+    pos = np.array([top, top - 511, (1 << 29) + 7, 512])
+    desc_, inp, ck, cv, cache, out, pos = run_decode("sliding", 4, 16, 4, pos, 512, "ring", 160, 161)
+    ref, slots, k_hat = oracle_decode(desc_, inp, ck, cv, pos, "ring")
+    check("decode at positions near 2^30", out.cpu(), ref)
+    check_decode_cache(cache, inp, slots, k_hat)
+    # a 300-token prefill ending at 2^30 - 1 over a full ring
+    S = 300
+    desc_, inp, ck, cv, cache, out = run_prefill("sliding", 1, S, 16, 4, [top + 1 - S], 162, "ring", 512,
+                                                 hist_seed=163)
+    ref, _ = oracle_prefill(desc_, inp, ck, cv, [top + 1 - S], "ring", 512)
+    check("prefill ending at 2^30 - 1", out.cpu(), ref)
+    # 128 sequences of 0..9 new tokens in one ragged call (full layer, 8/2 heads)
+    rng = np.random.default_rng(164)
+    lens = [int(x) for x in rng.integers(0, 10, 128)]
+    starts = [int(x) for x in rng.integers(0, 200, 128)]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    fdesc = hb.layer_desc("full", 8, 2)
+    pin = {n: t[0] for n, t in synth.prefill_inputs(1, T, 8, 2, seed=165).items()}
+    fk = synth.cache_tensor(128, 2, 256, seed=166)
+    fv = synth.cache_tensor(128, 2, 256, seed=167)
+    fc = hb.KVCache(fk.to(DEV), fv.to(DEV), "linear")
+    d = to_dev(pin)
+    o = hb.hattn_prefill_varlen(fdesc, d["q"], d["k"], d["v"], d["gate"], cu, starts, fc)
+    torch.cuda.synchronize()
+    hk, hv, hp = history_for("linear", fk, fv, starts, 256)
+    ref, _ = O.prefill_varlen_ref(pin["q"], pin["k"], pin["v"], pin["gate"], cu, starts, window=None,
+                                  theta=fdesc.rope_theta, rotary_fraction=fdesc.rotary_fraction, hist_k=hk, hist_v=hv,
+                                  hist_pos=hp)
+    check("ragged prefill of 128 sequences", o.cpu(), ref)
