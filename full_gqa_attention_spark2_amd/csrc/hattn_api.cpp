@@ -506,8 +506,10 @@ int decode_strided(const hattn_layer_desc* desc, const void* q, const void* k, c
   if (cache->kind != HATTN_KV_RING && max_pos >= cache->capacity) return HATTN_ERR_CAPACITY;
   const long long span = decode_span(desc, cache, max_pos);
   const DecodePlan p = decode_plan(desc, cache, batch, span);
-  // one-dimensional grids: (sequences x KV heads x splits) and (sequences x heads)
-  if ((long long)batch * desc->num_kv_heads * p.nsplit > INT32_MAX || (long long)batch * desc->num_q_heads > INT32_MAX)
+  // one-dimensional grids: (sequences x KV heads x splits) and (sequences x
+  // heads x 4 channel quarters)
+  if ((long long)batch * desc->num_kv_heads * p.nsplit > INT32_MAX ||
+      (long long)batch * desc->num_q_heads * 4 > INT32_MAX)
     return HATTN_ERR_UNSUPPORTED;
   const size_t parts = (size_t)batch * desc->num_q_heads * p.nsplit;
   const size_t o_bytes = align_up(parts * desc->head_dim * 4, 256);

@@ -457,24 +457,30 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
 }
 
 // Merge of the split partials, gate, bf16 store. One block per (sequence,
-// head): the block first turns every split's (m, l) into a weight
-// 2^(m_s - M) and the total L, then 4 thread groups each sum a quarter of the
-// splits' partial outputs (8 loads in flight per thread) and combine in a
-// fixed order, so the result does not depend on timing.
+// head, quarter of the channels), so even a single sequence spreads over
+// 64 blocks: the block turns every split's (m, l) into a weight 2^(m_s - M)
+// and the total L, then 16 thread groups each sum every 16th split for the
+// block's 64 channels (8 loads in flight per thread) and combine in a fixed
+// order, so the result does not depend on timing.
 constexpr int kMergeThreads = 1024;
 constexpr int kMaxSplits = 2048;
+constexpr int kMergeChannels = 64;                          // channels per block
+constexpr int kMergeGroups = kMergeThreads / kMergeChannels;  // split groups per block
+constexpr int kMergeBlocksPerHead = kHeadDim / kMergeChannels;
 
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a) {
   __shared__ float wgt[kMaxSplits];
   __shared__ float red[kMergeThreads / 64];
-  __shared__ float part[3][kHeadDim];
-  const int b = (int)blockIdx.x / a.Hq;
-  const int h = (int)blockIdx.x % a.Hq;
+  __shared__ float part[kMergeGroups][kMergeChannels];
+  const int bh = (int)blockIdx.x / kMergeBlocksPerHead;
+  const int c0 = ((int)blockIdx.x % kMergeBlocksPerHead) * kMergeChannels;
+  const int b = bh / a.Hq;
+  const int h = bh % a.Hq;
   const int t = threadIdx.x;
   const int p = a.pos[b];
-  uint16_t* o = a.out + ((size_t)b * a.Hq + h) * kHeadDim;
+  uint16_t* o = a.out + ((size_t)b * a.Hq + h) * kHeadDim + c0;
   if (p < 0 || p > a.max_pos) {
-    if (t < kHeadDim) o[t] = 0x7fc0;
+    if (t < kMergeChannels) o[t] = 0x7fc0;
     return;
   }
   const size_t base = ((size_t)b * a.Hq + h) * a.nsplit;
@@ -499,24 +505,27 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   __syncthreads();
   float L = 0.f;
   for (int i = 0; i < kMergeThreads / 64; ++i) L += red[i];
-  // O[d] = sum_s w_s o_s[d]; thread group g takes splits g, g+4, ...
-  const int g = t >> 8, d = t & 255;
+  // O[d] = sum_s w_s o_s[d]; thread group g takes splits g, g + 16, ...
+  const int g = t / kMergeChannels, dl = t % kMergeChannels;
+  const float* po = a.part_o + base * kHeadDim + c0 + dl;
   float acc = 0.f;
   int s = g;
-  for (; s + 28 < a.nsplit; s += 32) {
+  for (; s + 7 * kMergeGroups < a.nsplit; s += 8 * kMergeGroups) {
     float v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = a.part_o[(base + s + 4 * u) * kHeadDim + d];
+    for (int u = 0; u < 8; ++u) v[u] = po[(size_t)(s + kMergeGroups * u) * kHeadDim];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc += wgt[s + 4 * u] * v[u];
+    for (int u = 0; u < 8; ++u) acc += wgt[s + kMergeGroups * u] * v[u];
   }
-  for (; s < a.nsplit; s += 4) acc += wgt[s] * a.part_o[(base + s) * kHeadDim + d];
-  if (g > 0) part[g - 1][d] = acc;
+  for (; s < a.nsplit; s += kMergeGroups) acc += wgt[s] * po[(size_t)s * kHeadDim];
+  part[g][dl] = acc;
   __syncthreads();
   if (g == 0) {
-    const float O = ((acc + part[0][d]) + part[1][d]) + part[2][d];
+    float O = part[0][dl];
+#pragma unroll
+    for (int i = 1; i < kMergeGroups; ++i) O += part[i][dl];
     const float gl = bf16_bits_to_float(a.gate[(size_t)b * a.gate_stride + h]);
-    o[d] = float_to_bf16_bits(O / L * gate_factor(gl, a.gate_act));
+    o[dl] = float_to_bf16_bits(O / L * gate_factor(gl, a.gate_act));
   }
 }
 
@@ -529,7 +538,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(decode_kernel<false>, dim3(grid), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(a.B * a.Hq), dim3(kMergeThreads), 0, s, a);
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(a.B * a.Hq * kMergeBlocksPerHead), dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();
 }
 
