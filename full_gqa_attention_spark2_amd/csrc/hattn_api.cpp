@@ -183,93 +183,20 @@ DecodePlan decode_plan(const hattn_layer_desc* d, const hattn_kv_cache* c, int B
   return DecodePlan{(int)n, (int)keys};
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* hattn_status_string(int status) {
-  switch (status) {
-    case HATTN_OK: return "ok";
-    case HATTN_ERR_NULL: return "null pointer";
-    case HATTN_ERR_SHAPE: return "invalid or inconsistent size";
-    case HATTN_ERR_UNSUPPORTED: return "unsupported head_dim or GQA group size";
-    case HATTN_ERR_ROPE: return "invalid RoPE theta or rotary fraction";
-    case HATTN_ERR_WINDOW: return "window does not match the layer type";
-    case HATTN_ERR_CACHE: return "cache kind, capacity or batch does not fit the layer";
-    case HATTN_ERR_CAPACITY: return "positions exceed the linear cache capacity";
-    case HATTN_ERR_WORKSPACE: return "workspace missing or too small";
-    case HATTN_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
-    case HATTN_ERR_LAUNCH: return "HIP launch failed";
-    case HATTN_ERR_POSITION: return "position out of range";
-    default: return "unknown status";
-  }
-}
-
-int hattn_layer_defaults(int32_t layer_type, int32_t num_q_heads, int32_t num_kv_heads,
-                         hattn_layer_desc* out) {
-  if (!out) return HATTN_ERR_NULL;
-  hattn_layer_desc d{};
-  d.layer_type = layer_type;
-  d.num_q_heads = num_q_heads;
-  d.num_kv_heads = num_kv_heads;
-  d.head_dim = kHeadDimSupported;
-  if (layer_type == HATTN_LAYER_SLIDING) {
-    d.window = 512;
-    d.rope_theta = 1.0e4;
-    d.rotary_fraction = 1.0;
-  } else if (layer_type == HATTN_LAYER_FULL) {
-    d.window = 0;
-    d.rope_theta = 5.0e6;
-    d.rotary_fraction = 0.25;
-  } else {
-    return HATTN_ERR_SHAPE;
-  }
-  const int st = check_desc(&d);
+// Checks shared by both prefill entry points (before any sequence data).
+int prefill_common_checks(const hattn_layer_desc* desc, const hattn_kv_cache* cache, int32_t batch,
+                          const int32_t* start_pos) {
+  int st = check_desc(desc);
   if (st != HATTN_OK) return st;
-  *out = d;
+  if (batch <= 0) return HATTN_ERR_SHAPE;
+  if (batch > kMaxPrefillBatch) return HATTN_ERR_UNSUPPORTED;
+  st = check_cache(desc, cache, batch);
+  if (st != HATTN_OK) return st;
+  if (!start_pos) return HATTN_ERR_NULL;
   return HATTN_OK;
 }
 
-int hattn_rope_apply(void* x, int32_t n_tok, int32_t n_heads, int32_t head_dim, const int32_t* pos,
-                     double theta, double rotary_fraction, hipStream_t stream) {
-  if (n_tok < 0 || n_heads <= 0 || head_dim <= 0 || head_dim % 2) return HATTN_ERR_SHAPE;
-  if (head_dim > 512) return HATTN_ERR_UNSUPPORTED;
-  if (!(theta > 0.0) || !isfinite(theta)) return HATTN_ERR_ROPE;
-  const int r = rotary_channels(rotary_fraction, head_dim);
-  if (r < 0) return HATTN_ERR_ROPE;
-  if (n_tok == 0) return HATTN_OK;
-  if (!x || !pos) return HATTN_ERR_NULL;
-  if (((uintptr_t)x & 1u) || ((uintptr_t)pos & 3u)) return HATTN_ERR_ALIGN;
-  RopeApplyArgs a{};
-  a.x = (uint16_t*)x;
-  a.pos = pos;
-  a.n_tok = n_tok;
-  a.n_heads = n_heads;
-  a.head_dim = head_dim;
-  a.r = r;
-  fill_inv_freq(theta, r, a.inv_freq);
-  return from_hip(launch_rope_apply(a, stream));
-}
-
-size_t hattn_prefill_workspace_size(const hattn_layer_desc* desc, const hattn_kv_cache* cache,
-                                    int32_t batch, int32_t seq_len) {
-  if (check_desc(desc) != HATTN_OK || !cache || batch <= 0 || seq_len < 0) return 0;
-  return prefill_layout(desc, cache, batch, (long long)batch * seq_len, seq_len).total;
-}
-
-size_t hattn_prefill_varlen_workspace_size(const hattn_layer_desc* desc, const hattn_kv_cache* cache,
-                                           int32_t batch, const int32_t* cu_seqlens) {
-  if (check_desc(desc) != HATTN_OK || !cache || batch <= 0 || !cu_seqlens || cu_seqlens[0] != 0) return 0;
-  int max_len = 0;
-  for (int b = 0; b < batch; ++b) {
-    const long long n = (long long)cu_seqlens[b + 1] - cu_seqlens[b];
-    if (n < 0) return 0;
-    max_len = std::max<int>(max_len, (int)n);
-  }
-  return prefill_layout(desc, cache, batch, cu_seqlens[batch], max_len).total;
-}
-
-}  // extern "C"
+}  // namespace
 
 namespace hattn {
 
@@ -411,82 +338,6 @@ int prefill_packed(const hattn_layer_desc* desc, const void* q, const void* k, c
   return HATTN_OK;
 }
 
-}  // namespace hattn
-
-namespace {
-
-// Checks shared by both prefill entry points (before any sequence data).
-int prefill_common_checks(const hattn_layer_desc* desc, const hattn_kv_cache* cache, int32_t batch,
-                          const int32_t* start_pos) {
-  int st = check_desc(desc);
-  if (st != HATTN_OK) return st;
-  if (batch <= 0) return HATTN_ERR_SHAPE;
-  if (batch > kMaxPrefillBatch) return HATTN_ERR_UNSUPPORTED;
-  st = check_cache(desc, cache, batch);
-  if (st != HATTN_OK) return st;
-  if (!start_pos) return HATTN_ERR_NULL;
-  return HATTN_OK;
-}
-
-}  // namespace
-
-extern "C" {
-
-int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
-                  const void* gate, int32_t batch, int32_t seq_len, const int32_t* start_pos,
-                  const hattn_kv_cache* cache, void* out, void* workspace, size_t workspace_bytes,
-                  hipStream_t stream) {
-  int st = check_desc(desc);
-  if (st != HATTN_OK) return st;
-  if (batch <= 0 || seq_len < 0) return HATTN_ERR_SHAPE;
-  st = prefill_common_checks(desc, cache, batch, start_pos);
-  if (st != HATTN_OK) return st;
-  if ((long long)batch * seq_len > INT32_MAX) return HATTN_ERR_UNSUPPORTED;
-  int tok0[kMaxPrefillBatch], len[kMaxPrefillBatch];
-  for (int b = 0; b < batch; ++b) {
-    tok0[b] = b * seq_len;
-    len[b] = seq_len;
-  }
-  return prefill_packed(desc, q, k, v, gate, batch, tok0, len, (long long)batch * seq_len, start_pos,
-                        cache, out, workspace, workspace_bytes, stream, (long long)desc->num_q_heads * kHeadDimSupported,
-                        (long long)desc->num_kv_heads * kHeadDimSupported, desc->num_q_heads);
-}
-
-int hattn_prefill_varlen(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
-                         const void* gate, int32_t batch, const int32_t* cu_seqlens,
-                         const int32_t* start_pos, const hattn_kv_cache* cache, void* out,
-                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  const int st = prefill_common_checks(desc, cache, batch, start_pos);
-  if (st != HATTN_OK) return st;
-  if (!cu_seqlens) return HATTN_ERR_NULL;
-  if (cu_seqlens[0] != 0) return HATTN_ERR_SHAPE;
-  int tok0[kMaxPrefillBatch], len[kMaxPrefillBatch];
-  for (int b = 0; b < batch; ++b) {
-    if (cu_seqlens[b + 1] < cu_seqlens[b]) return HATTN_ERR_SHAPE;
-    tok0[b] = cu_seqlens[b];
-    len[b] = cu_seqlens[b + 1] - cu_seqlens[b];
-  }
-  return prefill_packed(desc, q, k, v, gate, batch, tok0, len, cu_seqlens[batch], start_pos, cache, out,
-                        workspace, workspace_bytes, stream, (long long)desc->num_q_heads * kHeadDimSupported,
-                        (long long)desc->num_kv_heads * kHeadDimSupported, desc->num_q_heads);
-}
-
-size_t hattn_decode_workspace_size(const hattn_layer_desc* desc, const hattn_kv_cache* cache,
-                                   int32_t batch) {
-  if (check_desc(desc) != HATTN_OK || !cache || batch <= 0 || cache->capacity < 1) return 0;
-  const long long span = cache->kind == HATTN_KV_RING
-                             ? cache->capacity
-                             : decode_span(desc, cache, (long long)cache->capacity - 1);
-  const DecodePlan p = decode_plan(desc, cache, batch, span);
-  if (p.nsplit == 1) return 256;  // no partials needed; keep a non-zero size
-  const size_t parts = (size_t)batch * desc->num_q_heads * p.nsplit;
-  return align_up(parts * desc->head_dim * 4, 256) + align_up(parts * 2 * 4, 256);
-}
-
-}  // extern "C"
-
-namespace hattn {
-
 // hattn_decode with sequence rows of q, k/v and gate q_stride, kv_stride and
 // gate_stride elements apart (dense: Hq * 256, Hkv * 256, Hq).
 int decode_strided(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
@@ -553,6 +404,139 @@ int decode_strided(const hattn_layer_desc* desc, const void* q, const void* k, c
 }  // namespace hattn
 
 extern "C" {
+
+const char* hattn_status_string(int status) {
+  switch (status) {
+    case HATTN_OK: return "ok";
+    case HATTN_ERR_NULL: return "null pointer";
+    case HATTN_ERR_SHAPE: return "invalid or inconsistent size";
+    case HATTN_ERR_UNSUPPORTED: return "unsupported head_dim or GQA group size";
+    case HATTN_ERR_ROPE: return "invalid RoPE theta or rotary fraction";
+    case HATTN_ERR_WINDOW: return "window does not match the layer type";
+    case HATTN_ERR_CACHE: return "cache kind, capacity or batch does not fit the layer";
+    case HATTN_ERR_CAPACITY: return "positions exceed the linear cache capacity";
+    case HATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case HATTN_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+    case HATTN_ERR_LAUNCH: return "HIP launch failed";
+    case HATTN_ERR_POSITION: return "position out of range";
+    default: return "unknown status";
+  }
+}
+
+int hattn_layer_defaults(int32_t layer_type, int32_t num_q_heads, int32_t num_kv_heads,
+                         hattn_layer_desc* out) {
+  if (!out) return HATTN_ERR_NULL;
+  hattn_layer_desc d{};
+  d.layer_type = layer_type;
+  d.num_q_heads = num_q_heads;
+  d.num_kv_heads = num_kv_heads;
+  d.head_dim = kHeadDimSupported;
+  if (layer_type == HATTN_LAYER_SLIDING) {
+    d.window = 512;
+    d.rope_theta = 1.0e4;
+    d.rotary_fraction = 1.0;
+  } else if (layer_type == HATTN_LAYER_FULL) {
+    d.window = 0;
+    d.rope_theta = 5.0e6;
+    d.rotary_fraction = 0.25;
+  } else {
+    return HATTN_ERR_SHAPE;
+  }
+  const int st = check_desc(&d);
+  if (st != HATTN_OK) return st;
+  *out = d;
+  return HATTN_OK;
+}
+
+int hattn_rope_apply(void* x, int32_t n_tok, int32_t n_heads, int32_t head_dim, const int32_t* pos,
+                     double theta, double rotary_fraction, hipStream_t stream) {
+  if (n_tok < 0 || n_heads <= 0 || head_dim <= 0 || head_dim % 2) return HATTN_ERR_SHAPE;
+  if (head_dim > 512) return HATTN_ERR_UNSUPPORTED;
+  if (!(theta > 0.0) || !isfinite(theta)) return HATTN_ERR_ROPE;
+  const int r = rotary_channels(rotary_fraction, head_dim);
+  if (r < 0) return HATTN_ERR_ROPE;
+  if (n_tok == 0) return HATTN_OK;
+  if (!x || !pos) return HATTN_ERR_NULL;
+  if (((uintptr_t)x & 1u) || ((uintptr_t)pos & 3u)) return HATTN_ERR_ALIGN;
+  RopeApplyArgs a{};
+  a.x = (uint16_t*)x;
+  a.pos = pos;
+  a.n_tok = n_tok;
+  a.n_heads = n_heads;
+  a.head_dim = head_dim;
+  a.r = r;
+  fill_inv_freq(theta, r, a.inv_freq);
+  return from_hip(launch_rope_apply(a, stream));
+}
+
+size_t hattn_prefill_workspace_size(const hattn_layer_desc* desc, const hattn_kv_cache* cache,
+                                    int32_t batch, int32_t seq_len) {
+  if (check_desc(desc) != HATTN_OK || !cache || batch <= 0 || seq_len < 0) return 0;
+  return prefill_layout(desc, cache, batch, (long long)batch * seq_len, seq_len).total;
+}
+
+size_t hattn_prefill_varlen_workspace_size(const hattn_layer_desc* desc, const hattn_kv_cache* cache,
+                                           int32_t batch, const int32_t* cu_seqlens) {
+  if (check_desc(desc) != HATTN_OK || !cache || batch <= 0 || !cu_seqlens || cu_seqlens[0] != 0) return 0;
+  int max_len = 0;
+  for (int b = 0; b < batch; ++b) {
+    const long long n = (long long)cu_seqlens[b + 1] - cu_seqlens[b];
+    if (n < 0) return 0;
+    max_len = std::max<int>(max_len, (int)n);
+  }
+  return prefill_layout(desc, cache, batch, cu_seqlens[batch], max_len).total;
+}
+
+int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
+                  const void* gate, int32_t batch, int32_t seq_len, const int32_t* start_pos,
+                  const hattn_kv_cache* cache, void* out, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+  int st = check_desc(desc);
+  if (st != HATTN_OK) return st;
+  if (batch <= 0 || seq_len < 0) return HATTN_ERR_SHAPE;
+  st = prefill_common_checks(desc, cache, batch, start_pos);
+  if (st != HATTN_OK) return st;
+  if ((long long)batch * seq_len > INT32_MAX) return HATTN_ERR_UNSUPPORTED;
+  int tok0[kMaxPrefillBatch], len[kMaxPrefillBatch];
+  for (int b = 0; b < batch; ++b) {
+    tok0[b] = b * seq_len;
+    len[b] = seq_len;
+  }
+  return prefill_packed(desc, q, k, v, gate, batch, tok0, len, (long long)batch * seq_len, start_pos,
+                        cache, out, workspace, workspace_bytes, stream, (long long)desc->num_q_heads * kHeadDimSupported,
+                        (long long)desc->num_kv_heads * kHeadDimSupported, desc->num_q_heads);
+}
+
+int hattn_prefill_varlen(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
+                         const void* gate, int32_t batch, const int32_t* cu_seqlens,
+                         const int32_t* start_pos, const hattn_kv_cache* cache, void* out,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int st = prefill_common_checks(desc, cache, batch, start_pos);
+  if (st != HATTN_OK) return st;
+  if (!cu_seqlens) return HATTN_ERR_NULL;
+  if (cu_seqlens[0] != 0) return HATTN_ERR_SHAPE;
+  int tok0[kMaxPrefillBatch], len[kMaxPrefillBatch];
+  for (int b = 0; b < batch; ++b) {
+    if (cu_seqlens[b + 1] < cu_seqlens[b]) return HATTN_ERR_SHAPE;
+    tok0[b] = cu_seqlens[b];
+    len[b] = cu_seqlens[b + 1] - cu_seqlens[b];
+  }
+  return prefill_packed(desc, q, k, v, gate, batch, tok0, len, cu_seqlens[batch], start_pos, cache, out,
+                        workspace, workspace_bytes, stream, (long long)desc->num_q_heads * kHeadDimSupported,
+                        (long long)desc->num_kv_heads * kHeadDimSupported, desc->num_q_heads);
+}
+
+size_t hattn_decode_workspace_size(const hattn_layer_desc* desc, const hattn_kv_cache* cache,
+                                   int32_t batch) {
+  if (check_desc(desc) != HATTN_OK || !cache || batch <= 0 || cache->capacity < 1) return 0;
+  const long long span = cache->kind == HATTN_KV_RING
+                             ? cache->capacity
+                             : decode_span(desc, cache, (long long)cache->capacity - 1);
+  const DecodePlan p = decode_plan(desc, cache, batch, span);
+  if (p.nsplit == 1) return 256;  // no partials needed; keep a non-zero size
+  const size_t parts = (size_t)batch * desc->num_q_heads * p.nsplit;
+  return align_up(parts * desc->head_dim * 4, 256) + align_up(parts * 2 * 4, 256);
+}
 
 int hattn_decode(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
                  const void* gate, int32_t batch, const int32_t* pos, int32_t max_pos,
