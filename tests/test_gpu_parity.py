@@ -1,11 +1,14 @@
 """Parity of the HIP path (through the C ABI) with the CPU fp64 oracle.
 
 Bars: floating-point outputs within max-abs 1e-2 and relative RMS 3e-3 of
-the oracle; slots, positions and masks bit-exact; cached keys equal to the
-oracle's bf16-rounded rotated keys (a last-bit difference is allowed only on
-values that sit on a rounding boundary to within the two sides' fp64 cos/sin
-ulps, which the test bounds).
+the oracle (the headline workloads exactly; other cases widen each element's
+max-abs bar by what the bf16 store alone adds above |out| = 2, see
+store_allowance); slots, positions and masks bit-exact; cached keys equal to
+the oracle's bf16-rounded rotated keys (a last-bit difference is allowed only
+on values that sit on a rounding boundary to within the two sides' fp64
+cos/sin ulps, which the test bounds).
 """
+import os
 import sys
 
 import numpy as np
@@ -1079,3 +1082,46 @@ def test_largest_positions_and_batch():
                                   theta=fdesc.rope_theta, rotary_fraction=fdesc.rotary_fraction, hist_k=hk, hist_v=hv,
                                   hist_pos=hp)
     check("ragged prefill of 128 sequences", o.cpu(), ref)
+
+
+_SERIAL_SCRIPT = r"""
+import sys, numpy as np, torch
+sys.path.insert(0, sys.argv[1])
+from full_gqa_attention_spark2_amd import binding as hb, synth
+torch.cuda.set_device(0)
+dev = "cuda"
+desc = hb.layer_desc("full")
+inp = {k: v.to(dev) for k, v in synth.prefill_inputs(2, 200, 16, 4, seed=170).items()}
+cache = hb.KVCache.empty(2, 4, 4096, "linear")
+out = hb.hattn_prefill(desc, inp["q"], inp["k"], inp["v"], inp["gate"], [0, 3000], cache)
+d = {k: v.to(dev) for k, v in synth.decode_inputs(2, 16, 4, seed=171).items()}
+pos = torch.tensor([200, 3200], dtype=torch.int32, device=dev)
+dout = hb.hattn_decode(desc, d["q"], d["k"], d["v"], d["gate"], pos, 3200, cache)
+torch.cuda.synchronize()
+np.savez(sys.argv[2], prefill=out.view(torch.int16).cpu().numpy(), decode=dout.view(torch.int16).cpu().numpy(),
+         k=cache.k.view(torch.int16).cpu().numpy())
+"""
+
+
+def test_launch_blocking_rerun_is_bitwise_identical(tmp_path):
+    # the same prefill and decode (split plan, so two kernels) in a child
+    # process with every launch serialised (HIP_LAUNCH_BLOCKING=1) and in a
+    # child with the default asynchronous launches: a race between the
+    # library's kernels would show as a difference
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    script = tmp_path / "serial.py"
+    script.write_text(_SERIAL_SCRIPT)
+    res = {}
+    for tag, blocking in (("async", None), ("blocking", "1")):
+        env = dict(os.environ)
+        env.pop("HIP_LAUNCH_BLOCKING", None)
+        if blocking:
+            env["HIP_LAUNCH_BLOCKING"] = blocking
+        f = tmp_path / f"{tag}.npz"
+        r = subprocess.run([sys.executable, str(script), root, str(f)], env=env, capture_output=True, text=True,
+                           timeout=240)
+        assert r.returncode == 0, r.stderr[-2000:]
+        res[tag] = np.load(f)
+    for name in ("prefill", "decode", "k"):
+        assert np.array_equal(res["async"][name], res["blocking"][name]), name
