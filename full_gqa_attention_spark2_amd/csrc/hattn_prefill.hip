@@ -99,6 +99,12 @@ constexpr int stream_length(int mode) { return mode == kStreamSPv ? 64 : 32; }
 constexpr int kRing = 4;  // fragment registers per operand kind
 // LDS reads run this many stream elements ahead of their MFMA
 constexpr int stream_ahead(int mode) { return mode == kStreamSPv ? 6 : 3; }
+// A fragment register is rewritten by the read of the same-kind element
+// kRing places later, so fewer than kRing same-kind reads may be ahead of
+// an MFMA (in the mixed stream the kinds alternate).
+static_assert(stream_ahead(kStreamS) < kRing && stream_ahead(kStreamPv) < kRing &&
+                  stream_ahead(kStreamSPv) / 2 < kRing,
+              "LDS read look-ahead overruns the fragment register ring");
 constexpr int stream_reads(int mode, int e) {  // LDS reads feeding element e
   return mode == kStreamS ? 1 : mode == kStreamPv ? 2 : ((e & 1) ? 2 : 1);
 }
