@@ -20,10 +20,12 @@
 // whole 128-byte lines) in a swizzled layout that keeps the MFMA fragment
 // reads free of bank conflicts. Two K slots and two V slots form a pipeline:
 // step t runs S(t+1) and P(t-1).V(t-1) on the matrix cores while the VALU
-// computes the softmax of tile t, and K(t+2) and V(t) load meanwhile. The
-// running max is only moved (and O rescaled) when a tile's max exceeds it by
-// more than 2^8, so most tiles skip the rescale; the step body has no branch
-// between its MFMAs and its softmax.
+// computes the softmax of tile t, and K(t+2) and V(t) load meanwhile. Each
+// wave issues its share of those loads at its own point of the matrix-core
+// stream (wave w before element kLoadSpacing * w): the CU's load pipe takes
+// the four shares one after another, so no wave waits behind the others'.
+// The running max is only moved (and O rescaled) when a tile's max exceeds
+// it by more than 2^8, so most tiles skip the rescale.
 #include <type_traits>
 
 #include "hattn_device.h"
@@ -105,6 +107,10 @@ constexpr int stream_ahead(int mode) { return mode == kStreamSPv ? 6 : 3; }
 static_assert(stream_ahead(kStreamS) < kRing && stream_ahead(kStreamPv) < kRing &&
                   stream_ahead(kStreamSPv) / 2 < kRing,
               "LDS read look-ahead overruns the fragment register ring");
+// Stream elements between two waves' tile-load points. Every wave's point
+// must fall inside the shortest stream that carries loads (the first step's).
+constexpr int kLoadSpacing = 8;
+static_assert(4 * kLoadSpacing <= stream_length(kStreamS), "a wave's tile loads would never be issued");
 constexpr int stream_reads(int mode, int e) {  // LDS reads feeding element e
   return mode == kStreamS ? 1 : mode == kStreamPv ? 2 : ((e & 1) ? 2 : 1);
 }
@@ -386,7 +392,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   // scheduling-group barriers placed after the step's code (issue_order)
   // hold the compiler to that order, so every read has several MFMAs to land.
   auto mma_stream = [&](auto mode, const char* kslot, const char* vslot, f32x16& s0, f32x16& s1,
-                        const bf16x8* p) __attribute__((always_inline)) {
+                        const bf16x8* p, auto&& before) __attribute__((always_inline)) {
     constexpr bool kS = decltype(mode)::value != kStreamPv;
     constexpr bool kP = decltype(mode)::value != kStreamS;
     constexpr int kN = stream_length(decltype(mode)::value);
@@ -415,6 +421,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
     for (int e = 0; e < kAhead; ++e) issue(e);
 #pragma unroll
     for (int e = 0; e < kN; ++e) {
+      before(e);  // work placed ahead of element e (the tile loads)
       if (e + kAhead < kN) issue(e + kAhead);
       const int i = index(e);
       if (is_s(e)) {
@@ -497,13 +504,14 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   bf16x8 pA[4], pB[4];        // probabilities of even / odd tiles
   wait_loads();
   __syncthreads();
-  mma_stream(ModeS{}, k_lds0, v_lds0, sA0, sA1, pA);
+  mma_stream(ModeS{}, k_lds0, v_lds0, sA0, sA1, pA, [](int) {});
   issue_order<kStreamS, 0>();
   if (need_mask(t_lo)) mask_s(t_lo, sA0, sA1);
 
   // One iteration; the first one has no P.V yet. On the last tile S(t+1)
   // is computed from a stale slot and discarded, which keeps the body free
-  // of branches between its MFMAs and its softmax.
+  // of data-dependent branches between its MFMAs and its softmax (the only
+  // branches are the uniform ones around each wave's tile loads).
   auto step = [&](auto mode, int j, const char* kn, const char* vp, char* kf, char* vf, f32x16& sc0,
                   f32x16& sc1, f32x16& sn0, f32x16& sn1, const bf16x8* pp,
                   bf16x8* pn) __attribute__((always_inline)) {
@@ -511,14 +519,22 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
     const int t = t_lo + j;
     wait_loads();
     __syncthreads();
-    if (j + 2 < nt) load_k(t + 2, kf);
-    load_v(t, vf);
+    auto load_tiles = [&]() __attribute__((always_inline)) {
+      if (j + 2 < nt) load_k(t + 2, kf);
+      load_v(t, vf);
+    };
+    // The paged form keeps its loads at the step's start: its page lookups
+    // need scalar registers that the staggered placement would spill.
+    if constexpr (kPaged) load_tiles();
     // O holds P.V up to tile t-2 plus (below) tile t-1, all relative to the
     // max before softmax(t-1); a max move found by softmax(t-1) is applied
-    // here, before P(t-1).V(t-1) is added, keeping the stream and the
-    // softmax in one branch-free block.
+    // here, before P(t-1).V(t-1) is added, so no branch on the max sits
+    // inside the stream.
     if (rescale_pending) rescale_o(alpha_pending);
-    mma_stream(mode, kn, vp, sn0, sn1, pp);
+    mma_stream(mode, kn, vp, sn0, sn1, pp, [&](int e) __attribute__((always_inline)) {
+      if constexpr (!kPaged)
+        if (e % kLoadSpacing == 0 && e < 4 * kLoadSpacing && wave == e / kLoadSpacing) load_tiles();
+    });
     rescale_pending = softmax(sc0, sc1, pn, alpha_pending);
     issue_order<kMode, kSoftmaxValuPerMfma>();
     if (j + 1 < nt && need_mask(t + 1)) mask_s(t + 1, sn0, sn1);
@@ -534,10 +550,10 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   __syncthreads();
   if (rescale_pending) rescale_o(alpha_pending);
   if ((nt - 1) & 1) {
-    mma_stream(ModePv{}, k_lds0, v_lds1, sA0, sA1, pB);
+    mma_stream(ModePv{}, k_lds0, v_lds1, sA0, sA1, pB, [](int) {});
     issue_order<kStreamPv, 0>();
   } else {
-    mma_stream(ModePv{}, k_lds0, v_lds0, sA0, sA1, pA);
+    mma_stream(ModePv{}, k_lds0, v_lds0, sA0, sA1, pA, [](int) {});
     issue_order<kStreamPv, 0>();
   }
   l_i = pair_sum(l_i);
