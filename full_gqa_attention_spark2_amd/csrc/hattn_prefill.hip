@@ -519,20 +519,22 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
     const int t = t_lo + j;
     wait_loads();
     __syncthreads();
+    // Page lookups (paged caches) at the step's start; each wave's loads at
+    // its own point of the stream. Without a K load (the last two steps)
+    // the K lookup takes tile t, whose page is staged.
+    const int tk = j + 2 < nt ? t + 2 : t;
+    const __amdgpu_buffer_rsrc_t rk = kPaged ? page_rsrc(a.kc, tk) : krs;
+    const __amdgpu_buffer_rsrc_t rv = kPaged ? page_rsrc(a.vc, t) : vrs;
     auto load_tiles = [&]() __attribute__((always_inline)) {
-      if (j + 2 < nt) load_k(t + 2, kf);
-      load_v(t, vf);
+      if (j + 2 < nt) load_tile(rk, k_chunk0, k_chunk1, t + 2, kf);
+      load_tile(rv, v_chunk, v_chunk, t, vf);
     };
-    // The paged form keeps its loads at the step's start: its page lookups
-    // need scalar registers that the staggered placement would spill.
-    if constexpr (kPaged) load_tiles();
     // O holds P.V up to tile t-2 plus (below) tile t-1, all relative to the
     // max before softmax(t-1); a max move found by softmax(t-1) is applied
     // here, before P(t-1).V(t-1) is added, so no branch on the max sits
     // inside the stream.
     if (rescale_pending) rescale_o(alpha_pending);
     mma_stream(mode, kn, vp, sn0, sn1, pp, [&](int e) __attribute__((always_inline)) {
-      if constexpr (!kPaged)
         if (e % kLoadSpacing == 0 && e < 4 * kLoadSpacing && wave == e / kLoadSpacing) load_tiles();
     });
     rescale_pending = softmax(sc0, sc1, pn, alpha_pending);
