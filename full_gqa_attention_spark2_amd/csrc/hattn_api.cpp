@@ -59,10 +59,10 @@ int check_desc(const hattn_layer_desc* d) {
   return HATTN_OK;
 }
 
-int check_cache(const hattn_layer_desc* d, const hattn_kv_cache* c, int batch) {
+// The cache's kind, batch, capacity and paging against the layer (no
+// pointer checks: the workspace-size queries take a described cache).
+int check_cache_shape(const hattn_layer_desc* d, const hattn_kv_cache* c, int batch) {
   if (!c) return HATTN_ERR_NULL;
-  if (!c->k || !c->v) return HATTN_ERR_NULL;
-  if (!aligned16(c->k) || !aligned16(c->v)) return HATTN_ERR_ALIGN;
   if (c->batch != batch || c->capacity < 1) return HATTN_ERR_CACHE;
   if (c->kind == HATTN_KV_RING) {
     if (d->layer_type != HATTN_LAYER_SLIDING || c->capacity != d->window) return HATTN_ERR_CACHE;
@@ -72,10 +72,21 @@ int check_cache(const hattn_layer_desc* d, const hattn_kv_cache* c, int batch) {
     if (c->page_size < kMinPageSize || c->page_size % kMinPageSize || c->capacity % c->page_size)
       return HATTN_ERR_CACHE;
     if (c->capacity / c->page_size > kMaxPagesPerSeq || c->num_pages < 1) return HATTN_ERR_CACHE;
-    if (!c->block_table) return HATTN_ERR_NULL;
-    if ((uintptr_t)c->block_table & 3u) return HATTN_ERR_ALIGN;
   } else if (c->kind != HATTN_KV_LINEAR) {
     return HATTN_ERR_CACHE;
+  }
+  return HATTN_OK;
+}
+
+// check_cache_shape plus the cache's pointers.
+int check_cache(const hattn_layer_desc* d, const hattn_kv_cache* c, int batch) {
+  const int st = check_cache_shape(d, c, batch);
+  if (st != HATTN_OK) return st;
+  if (!c->k || !c->v) return HATTN_ERR_NULL;
+  if (!aligned16(c->k) || !aligned16(c->v)) return HATTN_ERR_ALIGN;
+  if (c->kind == HATTN_KV_PAGED) {
+    if (!c->block_table) return HATTN_ERR_NULL;
+    if ((uintptr_t)c->block_table & 3u) return HATTN_ERR_ALIGN;
   }
   return HATTN_OK;
 }
@@ -183,6 +194,23 @@ DecodePlan decode_plan(const hattn_layer_desc* d, const hattn_kv_cache* c, int B
   return DecodePlan{(int)n, (int)keys};
 }
 
+// The most splits decode_plan gives for any visible span up to `span`: its
+// split count is at most min(target, ceil(span / 128), limit), a bound that
+// grows with span (the count itself need not: rounding the keys per split
+// up to 128 can lower it at a larger span).
+long long decode_max_splits(const hattn_layer_desc* d, int B, long long span) {
+  const long long base = (long long)B * d->num_kv_heads;
+  if (base >= kDecodeWidePairs) return 1;
+  const long long want = (kDecodeTargetBlocks + base - 1) / base;
+  return std::max<long long>(1, std::min({want, (span + 127) / 128, (long long)kMaxDecodeSplits}));
+}
+
+// Bytes of the split partials (o, then (m, l)) for n splits.
+size_t decode_partials_bytes(const hattn_layer_desc* d, int B, long long n) {
+  const size_t parts = (size_t)B * d->num_q_heads * (size_t)n;
+  return align_up(parts * d->head_dim * 4, 256) + align_up(parts * 2 * 4, 256);
+}
+
 // Checks shared by both prefill entry points (before any sequence data).
 int prefill_common_checks(const hattn_layer_desc* desc, const hattn_kv_cache* cache, int32_t batch,
                           const int32_t* start_pos) {
@@ -199,6 +227,13 @@ int prefill_common_checks(const hattn_layer_desc* desc, const hattn_kv_cache* ca
 }  // namespace
 
 namespace hattn {
+
+int validate_layer_cache(const hattn_layer_desc* desc, const hattn_kv_cache* cache, int batch, bool pointers) {
+  const int st = check_desc(desc);
+  if (st != HATTN_OK) return st;
+  if (batch <= 0) return HATTN_ERR_SHAPE;
+  return pointers ? check_cache(desc, cache, batch) : check_cache_shape(desc, cache, batch);
+}
 
 size_t prefill_workspace_bytes(const hattn_layer_desc* desc, const hattn_kv_cache* cache, int batch,
                                long long total_tokens, int max_len) {
@@ -219,11 +254,14 @@ int prefill_packed(const hattn_layer_desc* desc, const void* q, const void* k, c
                    const int32_t* start_pos, const hattn_kv_cache* cache, void* out, void* workspace,
                    size_t workspace_bytes, hipStream_t stream, long long q_stride, long long kv_stride,
                    long long gate_stride) {
-  if (batch > kMaxPrefillBatch) return HATTN_ERR_UNSUPPORTED;
+  const int st = prefill_common_checks(desc, cache, batch, start_pos);
+  if (st != HATTN_OK) return st;
+  if (!tok0 || !len) return HATTN_ERR_NULL;
   const bool ring = cache->kind == HATTN_KV_RING;
   int max_len = 0;
   for (int b = 0; b < batch; ++b) {
     const long long s0 = start_pos[b];
+    if (len[b] < 0) return HATTN_ERR_SHAPE;
     if (s0 < 0 || s0 + len[b] > kMaxPos) return HATTN_ERR_POSITION;
     if (!ring && s0 + len[b] > cache->capacity) return HATTN_ERR_CAPACITY;
     max_len = std::max(max_len, len[b]);
@@ -364,7 +402,7 @@ int decode_strided(const hattn_layer_desc* desc, const void* q, const void* k, c
     return HATTN_ERR_UNSUPPORTED;
   const size_t parts = (size_t)batch * desc->num_q_heads * p.nsplit;
   const size_t o_bytes = align_up(parts * desc->head_dim * 4, 256);
-  const size_t need = p.nsplit == 1 ? 0 : o_bytes + align_up(parts * 2 * 4, 256);
+  const size_t need = p.nsplit == 1 ? 0 : decode_partials_bytes(desc, batch, p.nsplit);
   if (need > 0 && (!workspace || workspace_bytes < need)) return HATTN_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return HATTN_ERR_ALIGN;
 
@@ -471,13 +509,16 @@ int hattn_rope_apply(void* x, int32_t n_tok, int32_t n_heads, int32_t head_dim, 
 
 size_t hattn_prefill_workspace_size(const hattn_layer_desc* desc, const hattn_kv_cache* cache,
                                     int32_t batch, int32_t seq_len) {
-  if (check_desc(desc) != HATTN_OK || !cache || batch <= 0 || seq_len < 0) return 0;
+  if (check_desc(desc) != HATTN_OK || batch <= 0 || seq_len < 0 || check_cache_shape(desc, cache, batch) != HATTN_OK)
+    return 0;
   return prefill_layout(desc, cache, batch, (long long)batch * seq_len, seq_len).total;
 }
 
 size_t hattn_prefill_varlen_workspace_size(const hattn_layer_desc* desc, const hattn_kv_cache* cache,
                                            int32_t batch, const int32_t* cu_seqlens) {
-  if (check_desc(desc) != HATTN_OK || !cache || batch <= 0 || !cu_seqlens || cu_seqlens[0] != 0) return 0;
+  if (check_desc(desc) != HATTN_OK || batch <= 0 || check_cache_shape(desc, cache, batch) != HATTN_OK ||
+      !cu_seqlens || cu_seqlens[0] != 0)
+    return 0;
   int max_len = 0;
   for (int b = 0; b < batch; ++b) {
     const long long n = (long long)cu_seqlens[b + 1] - cu_seqlens[b];
@@ -528,14 +569,13 @@ int hattn_prefill_varlen(const hattn_layer_desc* desc, const void* q, const void
 
 size_t hattn_decode_workspace_size(const hattn_layer_desc* desc, const hattn_kv_cache* cache,
                                    int32_t batch) {
-  if (check_desc(desc) != HATTN_OK || !cache || batch <= 0 || cache->capacity < 1) return 0;
+  if (check_desc(desc) != HATTN_OK || batch <= 0 || check_cache_shape(desc, cache, batch) != HATTN_OK) return 0;
   const long long span = cache->kind == HATTN_KV_RING
                              ? cache->capacity
                              : decode_span(desc, cache, (long long)cache->capacity - 1);
-  const DecodePlan p = decode_plan(desc, cache, batch, span);
-  if (p.nsplit == 1) return 256;  // no partials needed; keep a non-zero size
-  const size_t parts = (size_t)batch * desc->num_q_heads * p.nsplit;
-  return align_up(parts * desc->head_dim * 4, 256) + align_up(parts * 2 * 4, 256);
+  const long long n = decode_max_splits(desc, batch, span);
+  if (n == 1) return 256;  // no partials needed; keep a non-zero size
+  return decode_partials_bytes(desc, batch, n);
 }
 
 int hattn_decode(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,

@@ -210,7 +210,9 @@ extern "C" {
 
 size_t hattn_block_prefill_workspace_size(const hattn_layer_desc* desc, const hattn_block_weights* w,
                                           const hattn_kv_cache* cache, int32_t batch, const int32_t* cu_seqlens) {
-  if (check_weights(desc, w) != HATTN_OK || !cache || batch <= 0 || !cu_seqlens || cu_seqlens[0] != 0) return 0;
+  if (check_weights(desc, w) != HATTN_OK || validate_layer_cache(desc, cache, batch, false) != HATTN_OK ||
+      batch > kMaxPrefillBatch || !cu_seqlens || cu_seqlens[0] != 0)
+    return 0;
   int max_len = 0;
   for (int b = 0; b < batch; ++b) {
     if (cu_seqlens[b + 1] < cu_seqlens[b]) return 0;
@@ -225,9 +227,10 @@ int hattn_block_prefill(const hattn_layer_desc* desc, const hattn_block_weights*
                         void* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int st = check_weights(desc, w);
   if (st != HATTN_OK) return st;
-  if (batch <= 0) return HATTN_ERR_SHAPE;
+  st = validate_layer_cache(desc, cache, batch, true);
+  if (st != HATTN_OK) return st;
   if (batch > kMaxPrefillBatch) return HATTN_ERR_UNSUPPORTED;
-  if (!cu_seqlens || !start_pos || !cache) return HATTN_ERR_NULL;
+  if (!cu_seqlens || !start_pos) return HATTN_ERR_NULL;
   if (cu_seqlens[0] != 0) return HATTN_ERR_SHAPE;
   int tok0[kMaxPrefillBatch], len[kMaxPrefillBatch], max_len = 0;
   for (int b = 0; b < batch; ++b) {
@@ -254,7 +257,7 @@ int hattn_block_prefill(const hattn_layer_desc* desc, const hattn_block_weights*
 
 size_t hattn_block_decode_workspace_size(const hattn_layer_desc* desc, const hattn_block_weights* w,
                                          const hattn_kv_cache* cache, int32_t batch) {
-  if (check_weights(desc, w) != HATTN_OK || !cache || batch <= 0) return 0;
+  if (check_weights(desc, w) != HATTN_OK || validate_layer_cache(desc, cache, batch, false) != HATTN_OK) return 0;
   return block_layout(desc, w, batch, decode_workspace_bytes(desc, cache, batch)).total;
 }
 
@@ -263,8 +266,8 @@ int hattn_block_decode(const hattn_layer_desc* desc, const hattn_block_weights* 
                        size_t workspace_bytes, hipStream_t stream) {
   int st = check_weights(desc, w);
   if (st != HATTN_OK) return st;
-  if (batch <= 0) return HATTN_ERR_SHAPE;
-  if (!cache) return HATTN_ERR_NULL;
+  st = validate_layer_cache(desc, cache, batch, true);
+  if (st != HATTN_OK) return st;
   if (!x || !out) return HATTN_ERR_NULL;
   if (!aligned16(x) || !aligned16(out) || !aligned16(workspace)) return HATTN_ERR_ALIGN;
   const size_t core_bytes = decode_workspace_bytes(desc, cache, batch);

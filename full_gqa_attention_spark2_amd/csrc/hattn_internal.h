@@ -158,6 +158,10 @@ int decode_strided(const hattn_layer_desc* desc, const void* q, const void* k, c
                    const void* gate, int32_t batch, const int32_t* pos, int32_t max_pos,
                    const hattn_kv_cache* cache, void* out, void* workspace, size_t workspace_bytes,
                    hipStream_t stream, long long q_stride, long long kv_stride, long long gate_stride);
+// The layer descriptor, a positive batch and the cache's kind, batch,
+// capacity and paging, as the public entry points check them; with
+// `pointers` also the cache's pointers. Returns a hattn_status.
+int validate_layer_cache(const hattn_layer_desc* desc, const hattn_kv_cache* cache, int batch, bool pointers);
 // Workspace bytes of prefill_packed / decode_strided.
 size_t prefill_workspace_bytes(const hattn_layer_desc* desc, const hattn_kv_cache* cache, int batch,
                                long long total_tokens, int max_len);

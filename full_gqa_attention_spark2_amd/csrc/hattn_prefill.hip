@@ -237,16 +237,13 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   auto load_k = [&](int t, char* slot) __attribute__((always_inline)) {
     load_tile(kPaged ? page_rsrc(a.kc, t) : krs, k_chunk0, k_chunk1, t, slot);
   };
-  auto load_v = [&](int t, char* slot) __attribute__((always_inline)) {
-    load_tile(kPaged ? page_rsrc(a.vc, t) : vrs, v_chunk, v_chunk, t, slot);
-  };
 
-  // The first tiles: requested right after the query loads below, so they
-  // are in flight during the query RoPE.
+  // The first K tiles: requested right after the query loads below, so they
+  // are in flight during the query RoPE. (V of the first tile is loaded by
+  // the first step, ahead of its P.V in the second.)
   auto load_first_tiles = [&]() __attribute__((always_inline)) {
     load_k(t_lo, k_lds0);
     if (nt > 1) load_k(t_lo + 1, k_lds1);
-    load_v(t_lo, v_lds0);
   };
 
   // ---- queries: RoPE in fp32 from the cos/sin table, then bf16 fragments

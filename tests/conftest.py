@@ -8,3 +8,12 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    import parity_log
+
+    if parity_log.LINES:
+        terminalreporter.write_sep("-", "headline parity errors (GPU vs the fp64 oracle)")
+        for line in parity_log.LINES:
+            terminalreporter.write_line(line)

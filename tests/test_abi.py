@@ -13,10 +13,11 @@ from full_gqa_attention_spark2_amd import binding as hb
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
-# Every call below is built to fail validation; on a machine with a GPU the
-# fake pointers would be dangerous if a check were missing, so these tests
-# only run where no GPU is visible.
-pytestmark = pytest.mark.skipif(torch.cuda.is_available(), reason="host-only ABI checks use fake pointers")
+# Most calls below are built to fail validation; on a machine with a GPU the
+# fake pointers would be dangerous if a check were missing, so those tests
+# only run where no GPU is visible. The export, status-string and
+# layer-default checks launch nothing and run everywhere.
+fake_pointers = pytest.mark.skipif(torch.cuda.is_available(), reason="host-only ABI checks use fake pointers")
 
 FAKE = 0x10000  # aligned, never dereferenced
 
@@ -66,6 +67,7 @@ def _decode(L, desc, cache, B=1, max_pos=10, ws_bytes=1 << 30, pos=FAKE):
                           ctypes.byref(cache), FAKE, FAKE, ws_bytes, None)
 
 
+@fake_pointers
 def test_prefill_rejects_bad_arguments(L):
     sl = hb.layer_desc("sliding")
     fu = hb.layer_desc("full")
@@ -112,6 +114,7 @@ def _varlen(L, desc, cache, cu, start, ws_bytes=1 << 30):
                                   None)
 
 
+@fake_pointers
 def test_paged_cache_validation(L):
     assert ctypes.sizeof(hb.KvCacheC) == 48
     fu = hb.layer_desc("full")
@@ -134,6 +137,7 @@ def test_paged_cache_validation(L):
     assert L.hattn_prefill_workspace_size(ctypes.byref(fu), ctypes.byref(paged()), 1, 100) == 100 * 32 * 8
 
 
+@fake_pointers
 def test_prefill_varlen_rejects_bad_arguments(L):
     fu = hb.layer_desc("full")
     lin = hb.KvCacheC(FAKE, FAKE, hb.KV_LINEAR, 3, 64)
@@ -158,6 +162,7 @@ def test_prefill_varlen_rejects_bad_arguments(L):
     assert got == 400 * 128 * 8 + 2 * 3 * 4 * (511 + 270) * 256 * 2
 
 
+@fake_pointers
 def test_block_rejects_bad_arguments(L):
     fu = hb.layer_desc("full")
     lin = hb.KvCacheC(FAKE, FAKE, hb.KV_LINEAR, 2, 4096)
@@ -188,7 +193,36 @@ def test_block_rejects_bad_arguments(L):
                                FAKE, 10, ctypes.byref(lin), FAKE, FAKE, 1 << 34, None)
     assert dec == -2
 
+    # the layer descriptor and the cache are validated before any workspace
+    # arithmetic or launch, in both block entry points
+    def pre_with(desc, cache):
+        return L.hattn_block_prefill(ctypes.byref(desc), ctypes.byref(good), FAKE, 2, ctypes.cast(cu, ctypes.c_void_p),
+                                     ctypes.cast(sp, ctypes.c_void_p), ctypes.byref(cache), FAKE, FAKE, 1 << 34, None)
 
+    def dec_with(desc, cache):
+        return L.hattn_block_decode(ctypes.byref(desc), ctypes.byref(good), FAKE, 2, FAKE, 10, ctypes.byref(cache),
+                                    FAKE, FAKE, 1 << 34, None)
+
+    sl = hb.layer_desc("sliding")
+    g2 = hb.layer_desc("full", 8, 2)
+    g2.num_kv_heads = 4                                                       # GQA group 2
+    bad = [
+        (g2, lin, -3),
+        (fu, hb.KvCacheC(FAKE, FAKE, hb.KV_LINEAR, 1, 4096), -6),           # cache batch 1 for B = 2
+        (sl, hb.KvCacheC(FAKE, FAKE, hb.KV_RING, 2, 100), -6),              # ring capacity != window
+        (fu, hb.KvCacheC(0, FAKE, hb.KV_LINEAR, 2, 4096), -1),              # null k
+        (fu, hb.KvCacheC(FAKE, FAKE, hb.KV_PAGED, 2, 4096, 256, 0, 64), -1),  # paged, null block table
+    ]
+    for desc, cache, want in bad:
+        assert pre_with(desc, cache) == want, (desc.num_kv_heads, cache.kind, cache.batch)
+        assert dec_with(desc, cache) == want, (desc.num_kv_heads, cache.kind, cache.batch)
+    assert L.hattn_block_prefill_workspace_size(ctypes.byref(g2), ctypes.byref(good), ctypes.byref(lin), 2,
+                                                ctypes.cast(cu, ctypes.c_void_p)) == 0
+    assert L.hattn_block_decode_workspace_size(ctypes.byref(fu), ctypes.byref(good),
+                                               ctypes.byref(hb.KvCacheC(FAKE, FAKE, hb.KV_LINEAR, 1, 4096)), 2) == 0
+
+
+@fake_pointers
 def test_decode_rejects_bad_arguments(L):
     sl = hb.layer_desc("sliding")
     fu = hb.layer_desc("full")
@@ -203,6 +237,7 @@ def test_decode_rejects_bad_arguments(L):
     assert _decode(L, fu, big, max_pos=(1 << 20) - 1, ws_bytes=100) == -8
 
 
+@fake_pointers
 def test_rope_apply_rejects_bad_arguments(L):
     f = L.hattn_rope_apply
     assert f(FAKE, 4, 2, 256, FAKE, 1e4, 0.3, None) == -4
@@ -214,6 +249,7 @@ def test_rope_apply_rejects_bad_arguments(L):
     assert f(0, 0, 2, 256, 0, 1e4, 1.0, None) == 0      # nothing to do
 
 
+@fake_pointers
 def test_workspace_sizes(L):
     fu = hb.layer_desc("full")
     sl = hb.layer_desc("sliding")
@@ -228,3 +264,31 @@ def test_workspace_sizes(L):
     big = hb.KvCacheC(FAKE, FAKE, hb.KV_LINEAR, 1, 1 << 20)
     assert L.hattn_decode_workspace_size(ctypes.byref(fu), ctypes.byref(big), 1) >= 16 * 2 * 256 * 4
     assert L.hattn_prefill_workspace_size(None, ctypes.byref(lin), 1, 8) == 0
+
+
+@fake_pointers
+@pytest.mark.parametrize("layer,kind,cap,B,Hq,Hkv", [
+    ("full", hb.KV_LINEAR, 266240, 2, 8, 2),     # the 1.7B full layer's 4096 + 262144 slots
+    ("full", hb.KV_LINEAR, 4100, 8, 16, 4),
+    ("full", hb.KV_LINEAR, 1 << 20, 1, 16, 4),
+    ("sliding", hb.KV_LINEAR, 300000, 50, 16, 4),
+    ("sliding", hb.KV_RING, 512, 3, 16, 4),
+])
+def test_decode_workspace_size_covers_every_position(L, layer, kind, cap, B, Hq, Hkv):
+    """The size query is an upper bound: a decode at any max_pos the cache
+    holds passes the workspace check with exactly that many bytes (here it
+    then reaches the launch, which fails without a GPU)."""
+    d = hb.layer_desc(layer, Hq, Hkv)
+    if layer == "sliding" and kind == hb.KV_LINEAR:
+        d.window = 1000
+    c = hb.KvCacheC(FAKE, FAKE, kind, B, cap)
+    ws = L.hattn_decode_workspace_size(ctypes.byref(d), ctypes.byref(c), B)
+    assert ws > 0
+    top = cap - 1 if kind != hb.KV_RING else (1 << 30) - 1
+    probes = sorted(set([0, 1, 127, 128, 129, 1000, 4095, 131071, 262143, 262144, top] +
+                        [int(x) for x in __import__("numpy").linspace(0, min(top, cap - 1 if kind != hb.KV_RING else 5000), 200)]))
+    for mp in probes:
+        if mp > top:
+            continue
+        st = _decode(L, d, c, B=B, max_pos=mp, ws_bytes=ws)
+        assert st in (0, -10), (mp, st)
