@@ -161,6 +161,137 @@ def to_paged(torch, hb, ck, cv, page, seed):
     return hb.KVCache.paged(pool(ck), pool(cv), perm.view(B, n).to(torch.int32).to(ck.device))
 
 
+class ClockSampler:
+    """Samples the GPU's shader clock from the driver's hwmon node
+    (freq1_input, Hz) on a background thread while a timed region runs.
+    Reports the mean and range of the samples, or why none were taken."""
+
+    def __init__(self, torch, dev, period_s=0.002):
+        import glob
+        import threading
+
+        self.period = period_s
+        self.samples = []
+        self.path = None
+        self.reason = None
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            props = torch.cuda.get_device_properties(dev)
+            bus = "%02x:%02x" % (props.pci_bus_id, props.pci_device_id)
+            for card in sorted(glob.glob("/sys/class/drm/card*/device")):
+                real = os.path.realpath(card)
+                if os.path.basename(real).split(":", 1)[-1].startswith(bus):
+                    hw = sorted(glob.glob(os.path.join(card, "hwmon", "hwmon*", "freq1_input")))
+                    if hw:
+                        self.path = hw[0]
+                    break
+            if self.path is None:
+                self.reason = f"no hwmon freq1_input for PCI bus {bus}"
+        except Exception as e:  # the sampler is optional: report why it is off
+            self.reason = f"{type(e).__name__}: {e}"
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                with open(self.path) as f:
+                    self.samples.append(int(f.read().strip()) / 1e9)
+            except (OSError, ValueError) as e:
+                self.reason = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+
+        if self.path:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread:
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return {"avg_GHz": None, "reason": self.reason or "no samples"}
+        x = self.samples
+        return {"avg_GHz": round(sum(x) / len(x), 3), "min_GHz": round(min(x), 3), "max_GHz": round(max(x), 3),
+                "samples": len(x), "source": self.path}
+
+
+def ceilings(torch, dev, steps=5):
+    """What plain vendor kernels reach on this GPU, timed beside the path:
+    torch.sum over 4 GiB of bf16 (a pure read), the same over 8 distinct
+    128 MiB buffers in turn (the sliding decode's size), and a bf16 GEMM of
+    8192^3 (hipBLASLt). Event-timed, back to back."""
+    res = {}
+    n4 = 1 << 31  # 4 GiB of bf16
+    big = torch.empty(n4, dtype=torch.bfloat16, device=dev).normal_()
+    ms = time_calls(torch, lambda: big.sum(dtype=torch.float32), steps, 2)
+    res["read_4GiB_torch_sum"] = {"ms": round(ms, 4), "GB_per_s": round(2 * n4 / (ms * 1e-3) / 1e9, 1)}
+    del big
+    sets = [torch.empty(1 << 26, dtype=torch.bfloat16, device=dev).normal_() for _ in range(8)]
+    it = [0]
+
+    def rd():
+        sets[it[0] % 8].sum(dtype=torch.float32)
+        it[0] += 1
+
+    ms = time_calls(torch, rd, 8 * steps, 8)
+    res["read_8x128MiB_torch_sum"] = {"us": round(ms * 1e3, 2), "GB_per_s": round((1 << 27) / (ms * 1e-3) / 1e9, 1)}
+    del sets
+    a = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    ms = time_calls(torch, lambda: torch.mm(a, b), steps, 2)
+    res["gemm_bf16_8192_torch_mm"] = {"ms": round(ms, 4), "TFLOP_per_s": round(2 * 8192 ** 3 / (ms * 1e-3) / 1e12, 1)}
+    del a, b
+    torch.cuda.empty_cache()
+    return res
+
+
+def chunked_stack(torch, hb, synth, dev, passes, warmup):
+    """The 1.7B shape's chunked prefill as one 28-layer pass: layers in the
+    page's order (sliding, sliding, sliding, full) x 7, each with its own
+    cache (21 rings of 512 slots, 7 linear caches of 266,240 slots holding
+    262,144 cached tokens), batch 2, 8 / 2 heads, a 4096-token chunk at
+    position 262,144. One event pair brackets each whole pass."""
+    B, S5, s0, Hq, Hkv = 2, 4096, 262144, 8, 2
+    order = ["full" if i % 4 == 3 else "sliding" for i in range(28)]
+    desc = {t: hb.layer_desc(t, Hq, Hkv) for t in ("sliding", "full")}
+    inp = {t: {k: v.to(dev) for k, v in synth.prefill_inputs(B, S5, Hq, Hkv, seed=40 + 10 * i).items()}
+           for i, t in enumerate(("sliding", "full"))}
+    out = {t: torch.empty_like(inp[t]["q"]) for t in inp}
+    ring_k = synth.cache_tensor(B, Hkv, 512, seed=41, threads=16).to(dev)
+    ring_v = synth.cache_tensor(B, Hkv, 512, seed=42, threads=16).to(dev)
+    lin_k = synth.cache_tensor(B, Hkv, s0 + S5, seed=51, fill_tokens=s0, threads=16).to(dev)
+    lin_v = synth.cache_tensor(B, Hkv, s0 + S5, seed=52, fill_tokens=s0, threads=16).to(dev)
+    caches = []
+    for t in order:
+        if t == "sliding":
+            caches.append(hb.KVCache(ring_k.clone(), ring_v.clone(), "ring"))
+        else:
+            caches.append(hb.KVCache(lin_k.clone(), lin_v.clone(), "linear"))
+    del ring_k, ring_v, lin_k, lin_v
+    ws = {t: torch.empty(max(hb.prefill_workspace_size(desc[t], caches[order.index(t)], B, S5), 256),
+                         dtype=torch.uint8, device=dev) for t in desc}
+    starts = [s0] * B
+
+    def one_pass():
+        for t, c in zip(order, caches):
+            d = inp[t]
+            hb.hattn_prefill(desc[t], d["q"], d["k"], d["v"], d["gate"], starts, c, out=out[t], workspace=ws[t])
+
+    t = time_each(torch, one_pass, passes, warmup)
+    fl = {tt: 4 * 256 * Hq * B * visible_pairs(S5, s0, window=512 if tt == "sliding" else None) for tt in desc}
+    flop = sum(fl[tt] for tt in order)
+    del caches, inp, out, ws
+    torch.cuda.empty_cache()
+    return t, flop, fl
+
+
 def time_calls(torch, fn, steps, warmup):
     for _ in range(warmup):
         fn()
@@ -191,11 +322,15 @@ def time_each(torch, fn, steps, warmup):
     return {"median": pick(0.5), "p10": pick(0.1), "p90": pick(0.9)}
 
 
-def cpu_baseline(S=8192, budget_s=12.0):
-    """The fp64 oracle on a bounded sample of the headline workload, on host
-    cores: interleaved sets of 512 evenly spaced query rows (rows k, k+16,
-    k+32, ... for k = 0, 1, ...) until about ``budget_s`` seconds of CPU work
-    are done or every row is covered."""
+def cpu_baseline(S=8192, budget_s=10.0, n_1m=1 << 20, s0=262144):
+    """The fp64 oracle, as it stands, on the host cores.
+
+    Headline (C2, the full-layer prefill of 8192 tokens): interleaved sets
+    of 512 evenly spaced query rows (rows k, k+16, k+32, ... for k = 0, 1,
+    ...) until about ``budget_s`` seconds of CPU work are done or every row
+    is covered. ``per_config`` times the oracle on the other workloads, each
+    on a stated bounded sample, in the unit of its GPU figure (TFLOP/s of
+    algorithmic attention work, or GB/s of KV read for decode)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -217,15 +352,86 @@ def cpu_baseline(S=8192, budget_s=12.0):
             break
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {
+    ncores = len(os.sched_getaffinity(0))
+    line = {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
         "sample": f"{done_rows} of the {S} query rows (interleaved sets of {S // stride} evenly spaced rows, "
                   f"all 16 heads, {flops / 1e9:.1f} GFLOP) of the full-layer prefill, fp64 numpy, "
-                  f"{dt:.1f} s on {len(os.sched_getaffinity(0))} visible host cores",
+                  f"{dt:.1f} s on {ncores} visible host cores",
     }
+    del inp
+    per = {}
+
+    def timed(fn):
+        t = time.perf_counter()
+        fn()
+        return time.perf_counter() - t
+
+    def exact64(t):
+        """The bf16 tensor's values as fp64 numpy (exact), prepared outside
+        the timed region so that only the oracle's arithmetic is timed."""
+        return t.float().numpy().astype(np.float64)
+
+    # C1: the whole sliding-layer prefill (1024 tokens from position 0)
+    c1 = synth.prefill_inputs(1, 1024, 16, 4, seed=30)
+    dt = timed(lambda: O.prefill_ref(c1["q"], c1["k"], c1["v"], c1["gate"], [0], window=512, theta=1e4,
+                                     rotary_fraction=1.0))
+    fl = 4 * 256 * 16 * visible_pairs(1024, 0, window=512)
+    per["sliding_s1024"] = {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "seconds": round(dt, 3),
+                            "sample": "the whole workload"}
+    # C3: the whole sliding decode (64 sequences, full 512-slot rings)
+    pos = synth.positions_uniform(64, 512, 1 << 20, seed=0).tolist()
+    d3 = synth.decode_inputs(64, 16, 4, seed=1)
+    rk = exact64(synth.cache_tensor(64, 4, 512, seed=100, threads=16))
+    rv = exact64(synth.cache_tensor(64, 4, 512, seed=101, threads=16))
+    dt = timed(lambda: O.decode_ref(d3["q"], d3["k"], d3["v"], d3["gate"], pos, rk, rv, kind="ring", window=512,
+                                    theta=1e4, rotary_fraction=1.0))
+    kv = 64 * 512 * 4 * 256 * 2 * 2
+    per["sliding_b64_ring512"] = {"value": round(kv / dt / 1e9, 3), "unit": "GB/s of KV", "seconds": round(dt, 3),
+                                  "sample": "the whole workload"}
+    del rk, rv
+    # C4a / C4b: one KV head (its 4 query heads) of the full-layer decode
+    for tag, n, note in (("full_b1_1M", n_1m, f"1 of the 4 KV heads (its 4 query heads) over {n_1m} positions"),
+                         ("full_b8_131072", 1 << 17, "1 of the 8 sequences, 1 of its 4 KV heads, over 131,072 "
+                                                     "positions")):
+        dq = synth.decode_inputs(1, 4, 1, seed=1)
+        ck = exact64(synth.cache_tensor(1, 1, n, seed=200, threads=16))
+        cv = exact64(synth.cache_tensor(1, 1, n, seed=201, threads=16))
+        dt = timed(lambda: O.decode_ref(dq["q"], dq["k"], dq["v"], dq["gate"], [n - 1], ck, cv, kind="linear",
+                                        window=None, theta=5e6, rotary_fraction=0.25))
+        kv = n * 256 * 2 * 2
+        per[tag] = {"value": round(kv / dt / 1e9, 3), "unit": "GB/s of KV", "seconds": round(dt, 3), "sample": note}
+        del ck, cv
+    # C5: 32 query rows of sequence 0 per layer type, all 8 heads, over the
+    # full history; extrapolated to the 28-layer pass (2 x 4096 rows per
+    # layer, 21 sliding + 7 full layers)
+    S5, nr = 4096, 32
+    rows = np.linspace(0, S5 - 1, nr).astype(np.int64)
+    c5 = synth.prefill_inputs(1, S5, 8, 2, seed=50)
+    hk = exact64(synth.cache_tensor(1, 2, s0, seed=51, threads=16))
+    hv = exact64(synth.cache_tensor(1, 2, s0, seed=52, threads=16))
+    hp = np.arange(s0, dtype=np.int64)[None]
+    dt_full = timed(lambda: O.prefill_ref(c5["q"], c5["k"], c5["v"], c5["gate"], [s0], window=None, theta=5e6,
+                                          rotary_fraction=0.25, hist_k=hk, hist_v=hv, hist_pos=hp, rows=rows))
+    del hk, hv
+    rk = exact64(synth.cache_tensor(1, 2, 511, seed=41, threads=16))
+    rv = exact64(synth.cache_tensor(1, 2, 511, seed=42, threads=16))
+    rp = np.arange(s0 - 511, s0, dtype=np.int64)[None]
+    dt_sl = timed(lambda: O.prefill_ref(c5["q"], c5["k"], c5["v"], c5["gate"], [s0], window=512, theta=1e4,
+                                        rotary_fraction=1.0, hist_k=rk, hist_v=rv, hist_pos=rp, rows=rows))
+    scale = 2 * S5 / nr
+    est = (7 * dt_full + 21 * dt_sl) * scale
+    fl28 = 2 * 4 * 256 * 8 * (7 * visible_pairs(S5, s0) + 21 * visible_pairs(S5, s0, window=512))
+    per["chunked_1p7b_28_layers"] = {
+        "value": round(fl28 / est / 1e12, 5), "unit": "TFLOP/s", "extrapolated_seconds_28_layers": round(est, 1),
+        "sample": f"{nr} query rows of sequence 0 for each layer type, all 8 heads, full history; extrapolated "
+                  f"x{scale:.0f} rows x (7 full + 21 sliding layers) (extrapolated)",
+        "measured_seconds": {"full_layer_rows": round(dt_full, 3), "sliding_layer_rows": round(dt_sl, 3)}}
+    line["per_config"] = per
+    return line
 
 
 def run(args):
@@ -258,7 +464,8 @@ def run(args):
     torch.cuda.synchronize()
     hb.hattn_profile_read(hb.PROFILE_PREFILL)
     hb.hattn_profile_enable(True)
-    ms = time_calls(torch, prefill, args.steps, 0)
+    with ClockSampler(torch, dev) as clk:
+        ms = time_calls(torch, prefill, args.steps, 0)
     hb.hattn_profile_enable(False)
     n, attn_total = hb.hattn_profile_read(hb.PROFILE_PREFILL)
     attn_ms = attn_total / max(n, 1)
@@ -271,6 +478,7 @@ def run(args):
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
         "traffic": counter_traffic("prefill_full_s8192"),
         "kernel": "prefill_attn_kernel", "flop_per_launch": flops, "avg_launch_ms": round(attn_ms, 5),
+        "launches_timed": n, "sclk_during_timed_steps": clk.summary(),
     }
     del inp, cache, out, ws
     torch.cuda.empty_cache()
@@ -307,16 +515,20 @@ def run(args):
         prefill_configs["sliding_s1024"] = {
             "us_per_call": {k: round(v * 1e3, 2) for k, v in t.items()}, "flop_per_call": fl,
             "TFLOP_per_s": round(tf, 2), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
-        # 1.7B shape: 8 / 2 heads, batch 2, a 4096-token chunk at 262144
+        # 1.7B shape: 8 / 2 heads, batch 2, a 4096-token chunk at 262144:
+        # the 28-layer pass measured as a whole, and each layer type alone
         s0, S5 = 262144, 4096
+        t28, fl28, _ = chunked_stack(torch, hb, synth, dev, max(5, args.steps // 4), 1)
+        ms28 = t28["median"]
+        tf28 = fl28 / (ms28 * 1e-3) / 1e12
+        log(f"prefill 1.7B chunk, 28-layer pass (measured): {ms28:.2f} ms median "
+            f"(p10 {t28['p10']:.2f}, p90 {t28['p90']:.2f}), {tf28:.1f} TFLOP/s")
         ts, fls = prefill_case("sliding", 2, S5, 8, 2, s0, 512, "ring", None, 40, 5, 2)
         torch.cuda.empty_cache()
         tfu, flf = prefill_case("full", 2, S5, 8, 2, s0, s0 + S5, "linear", s0, 50, 5, 2)
         torch.cuda.empty_cache()
-        ms28 = 21 * ts["median"] + 7 * tfu["median"]
-        fl28 = 21 * fls + 7 * flf
-        tf28 = fl28 / (ms28 * 1e-3) / 1e12
-        log(f"prefill 1.7B chunk (28 layers): {ms28:.2f} ms, {tf28:.1f} TFLOP/s "
+        ms28c = 21 * ts["median"] + 7 * tfu["median"]
+        log(f"prefill 1.7B chunk, composed 21 x sliding + 7 x full: {ms28c:.2f} ms "
             f"(sliding layer {ts['median']:.3f} ms, full layer {tfu['median']:.3f} ms)")
         # the same full-layer call on a paged cache (pages of 256 slots in a
         # shuffled pool)
@@ -331,7 +543,10 @@ def run(args):
         prefill_configs["chunked_1p7b_28_layers"] = {
             "ms_28_layers": round(ms28, 3), "flop_28_layers": fl28, "TFLOP_per_s": round(tf28, 2),
             "frac_bf16_peak": round(tf28 / PEAK_BF16_TFLOPS, 4),
-            "composed_from": "21 x sliding-layer call + 7 x full-layer call, medians",
+            "measured": "median of whole 28-layer passes (one event pair per pass) over 28 distinct caches",
+            "pass_ms": {k: round(v, 3) for k, v in t28.items()},
+            "composed_ms_28_layers": round(ms28c, 3),
+            "composed_from": "21 x sliding-layer call + 7 x full-layer call, medians (secondary)",
             "sliding_layer_ms": {k: round(v, 4) for k, v in ts.items()}, "sliding_layer_flop": fls,
             "full_layer_ms": {k: round(v, 4) for k, v in tfu.items()}, "full_layer_flop": flf,
             "full_layer_TFLOP_per_s": round(flf / (tfu["median"] * 1e-3) / 1e12, 2)}
@@ -364,6 +579,7 @@ def run(args):
 
             steps = max(args.steps, 2 * len(cs))
             ms_call = time_calls(torch, call, steps, args.warmup)
+            each = time_each(torch, call, max(steps, 3 * len(cs)), 0)
             win = min(cap, 512) if kind == "ring" else None
             toks = sum(min(p + 1, win) if win else p + 1 for p in pos)
             kv_bytes = toks * Hkv * 256 * 2 * 2
@@ -372,6 +588,7 @@ def run(args):
                 f"{gbps:.0f} GB/s, {gbps / PEAK_HBM_GBPS * 100:.1f}% of HBM peak")
             decode[tag] = {"GB_per_s": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
                            "kv_bytes_per_call": kv_bytes, "avg_call_us": round(ms_call * 1e3, 2),
+                           "per_call_us": {k: round(v * 1e3, 2) for k, v in each.items()},
                            "calls": steps, "distinct_caches": len(cs),
                            "traffic": counter_traffic("decode_" + tag)}
 
@@ -400,6 +617,10 @@ def run(args):
         del pg
         torch.cuda.empty_cache()
 
+    ceil = None if args.skip_ceilings else ceilings(torch, dev)
+    if ceil:
+        log(f"ceilings: {json.dumps(ceil)}")
+
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -420,6 +641,7 @@ def run(args):
             "flop_per_step": flops,
         },
         "roofline": roofline,
+        "practical_ceilings": ceil,
         "decode": decode,
         "prefill_configs": prefill_configs,
     }
@@ -437,6 +659,10 @@ def main(argv=None):
     ap.add_argument("--skip-prefill-configs", action="store_true",
                     help="skip the sliding 1024-token and 1.7B chunked prefill timings")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-ceilings", action="store_true",
+                    help="skip the plain torch read and GEMM timings")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only time the plain torch reads and GEMM (for kernel traces)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the copy of known size used to scale HBM counters")
     ap.add_argument("--block-only", action="store_true",
@@ -451,6 +677,9 @@ def main(argv=None):
         return 2
     if args.copy_calibration:
         line = copy_calibration()
+    elif args.ceilings:
+        import torch
+        line = ceilings(torch, torch.device("cuda:0"), steps=max(args.steps, 5))
     elif args.block_only:
         import torch
         from full_gqa_attention_spark2_amd import binding as hb, synth
