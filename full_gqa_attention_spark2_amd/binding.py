@@ -95,6 +95,8 @@ _SIGS = {
     "hattn_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc), ctypes.POINTER(KvCacheC), _I]),
     "hattn_decode": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _I, _P, _I,
                                     ctypes.POINTER(KvCacheC), _P, _P, ctypes.c_size_t, _P]),
+    "hattn_decode_static": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _I, _P, _I,
+                                           ctypes.POINTER(KvCacheC), _P, _P]),
     "hattn_block_prefill_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc), ctypes.POINTER(BlockWeightsC),
                                                              ctypes.POINTER(KvCacheC), _I, _P]),
     "hattn_block_prefill": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.POINTER(BlockWeightsC), _P, _I, _P, _P,
@@ -323,6 +325,29 @@ def hattn_decode(desc, q, k, v, gate, pos, max_pos, cache, out=None, workspace=N
     return out
 
 
+DECODE_STATIC_SCRATCH_BYTES = 6 << 20   # HATTN_DECODE_STATIC_SCRATCH_BYTES
+
+
+def hattn_decode_static(desc, q, k, v, gate, pos, max_pos, cache, out=None):
+    """hattn_decode with the library's static scratch instead of a
+    workspace (the call allocates nothing on the device; pass `out`)."""
+    B, Hq, D = q.shape
+    Hkv = k.shape[1]
+    _need(q, "q")
+    _need(k, "k", shape=(B, Hkv, D))
+    _need(v, "v", shape=(B, Hkv, D))
+    _need(gate, "gate", shape=(B, Hq))
+    _need(pos, "pos", torch.int32, (B,))
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", shape=q.shape)
+    cc = cache.c()
+    _check("hattn_decode_static", lib().hattn_decode_static(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), B, _ptr(pos), int(max_pos),
+        ctypes.byref(cc), _ptr(out), _stream(q.device)))
+    return out
+
+
 class BlockWeights:
     """Weights of one attention block on the GPU (bf16): the input RMSNorm
     weight [hidden], the fused projection [(Hq + 2 Hkv) * 256 + Hq, hidden]
@@ -459,3 +484,4 @@ def hattn_profile_read(kind):
     ms = ctypes.c_double()
     _check("hattn_profile_read", lib().hattn_profile_read(kind, ctypes.byref(n), ctypes.byref(ms)))
     return int(n.value), float(ms.value)
+

@@ -381,7 +381,8 @@ int prefill_packed(const hattn_layer_desc* desc, const void* q, const void* k, c
 int decode_strided(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
                    const void* gate, int32_t batch, const int32_t* pos, int32_t max_pos,
                    const hattn_kv_cache* cache, void* out, void* workspace, size_t workspace_bytes,
-                   hipStream_t stream, long long q_stride, long long kv_stride, long long gate_stride) {
+                   hipStream_t stream, long long q_stride, long long kv_stride, long long gate_stride,
+                   bool static_scratch) {
   int st = check_desc(desc);
   if (st != HATTN_OK) return st;
   if (batch <= 0) return HATTN_ERR_SHAPE;
@@ -403,6 +404,12 @@ int decode_strided(const hattn_layer_desc* desc, const void* q, const void* k, c
   const size_t parts = (size_t)batch * desc->num_q_heads * p.nsplit;
   const size_t o_bytes = align_up(parts * desc->head_dim * 4, 256);
   const size_t need = p.nsplit == 1 ? 0 : decode_partials_bytes(desc, batch, p.nsplit);
+  if (static_scratch) {
+    // the library's own array: its size bounds the plan, its address is
+    // looked up (no allocation) once the arguments are known to be valid
+    if (need > workspace_bytes) return HATTN_ERR_WORKSPACE;
+    if (need > 0 && decode_static_scratch(&workspace) != hipSuccess) return HATTN_ERR_LAUNCH;
+  }
   if (need > 0 && (!workspace || workspace_bytes < need)) return HATTN_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return HATTN_ERR_ALIGN;
 
@@ -587,6 +594,17 @@ int hattn_decode(const hattn_layer_desc* desc, const void* q, const void* k, con
   return decode_strided(desc, q, k, v, gate, batch, pos, max_pos, cache, out, workspace, workspace_bytes,
                         stream, (long long)desc->num_q_heads * kHeadDimSupported,
                         (long long)desc->num_kv_heads * kHeadDimSupported, desc->num_q_heads);
+}
+
+int hattn_decode_static(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
+                        const void* gate, int32_t batch, const int32_t* pos, int32_t max_pos,
+                        const hattn_kv_cache* cache, void* out, hipStream_t stream) {
+  const int st = check_desc(desc);
+  if (st != HATTN_OK) return st;
+  return decode_strided(desc, q, k, v, gate, batch, pos, max_pos, cache, out, nullptr,
+                        HATTN_DECODE_STATIC_SCRATCH_BYTES, stream, (long long)desc->num_q_heads * kHeadDimSupported,
+                        (long long)desc->num_kv_heads * kHeadDimSupported, desc->num_q_heads,
+                        /*static_scratch=*/true);
 }
 
 int hattn_profile_enable(int enable) {

@@ -20,8 +20,16 @@
 // caches, unbounded windows) each wave's first chunk is requested before the
 // position has arrived. The waves merge (m, l, o) in LDS; with several splits
 // a second kernel merges the splits in a fixed order.
+#include <mutex>
+
 #include "hattn_device.h"
 #include "hattn_internal.h"
+
+// Split partials of hattn_decode_static: one array per GPU, reserved with the
+// code object and kept until the process ends. Host code never passes the
+// symbol itself to a kernel: decode_static_scratch() looks up its device
+// address once per device.
+static __device__ __align__(256) unsigned char scratch[HATTN_DECODE_STATIC_SCRATCH_BYTES];
 
 namespace hattn {
 
@@ -527,6 +535,26 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
     const float gl = bf16_bits_to_float(a.gate[(size_t)b * a.gate_stride + h]);
     o[dl] = float_to_bf16_bits(O / L * gate_factor(gl, a.gate_act));
   }
+}
+
+hipError_t decode_static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {

@@ -148,7 +148,9 @@ namespace hattn {
 // The C-ABI prefill over packed new tokens (sequence b: rows tok0[b] ..
 // tok0[b] + len[b] - 1) and decode, with token rows of q, k/v and gate
 // q_stride, kv_stride and gate_stride elements apart. Validation as in the
-// public entry points; return a hattn_status.
+// public entry points; return a hattn_status. With static_scratch, decode
+// takes its split partials from the static array of hattn_decode_static
+// (workspace_bytes is that array's size; workspace is ignored).
 int prefill_packed(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
                    const void* gate, int32_t batch, const int* tok0, const int* len, long long total,
                    const int32_t* start_pos, const hattn_kv_cache* cache, void* out, void* workspace,
@@ -157,7 +159,8 @@ int prefill_packed(const hattn_layer_desc* desc, const void* q, const void* k, c
 int decode_strided(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
                    const void* gate, int32_t batch, const int32_t* pos, int32_t max_pos,
                    const hattn_kv_cache* cache, void* out, void* workspace, size_t workspace_bytes,
-                   hipStream_t stream, long long q_stride, long long kv_stride, long long gate_stride);
+                   hipStream_t stream, long long q_stride, long long kv_stride, long long gate_stride,
+                   bool static_scratch = false);
 // The layer descriptor, a positive batch and the cache's kind, batch,
 // capacity and paging, as the public entry points check them; with
 // `pointers` also the cache's pointers. Returns a hattn_status.
@@ -171,6 +174,9 @@ hipError_t launch_prefill_prep(const PrefillPrepArgs& a, hipStream_t s);
 hipError_t launch_ring_to_stage(const RingCopyArgs& a, hipStream_t s);
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// Device address of the current device's static decode scratch
+// (HATTN_DECODE_STATIC_SCRATCH_BYTES), looked up on first use per device.
+hipError_t decode_static_scratch(void** ptr);
 hipError_t launch_rope_apply(const RopeApplyArgs& a, hipStream_t s);
 hipError_t launch_index_probe(const ProbeArgs& a, hipStream_t s);
 hipError_t launch_rms_norm(const RmsNormArgs& a, hipStream_t s);

@@ -214,6 +214,27 @@ int hattn_decode(const hattn_layer_desc* desc, const void* q, const void* k,
                  const hattn_kv_cache* cache, void* out, void* workspace,
                  size_t workspace_bytes, hipStream_t stream);
 
+/* Decode without a caller workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation). Arguments, results and errors are those of
+ * hattn_decode; the split partials live instead in a library-owned device
+ * array of HATTN_DECODE_STATIC_SCRATCH_BYTES per GPU, reserved when the
+ * library is loaded and held until the process ends. Its device address is
+ * looked up once per device, on the first call with that device current (a
+ * symbol lookup, no allocation); the call itself makes no hipMalloc, hipFree
+ * or other allocating call. A plan needing more than the array returns
+ * HATTN_ERR_WORKSPACE (with a GQA group of 4 no plan does: at most
+ * 4 x (1024 + 255) partial rows of 1,032 bytes). Every call on a GPU shares
+ * that GPU's array and leaves its partials there; nothing in it needs to
+ * start at zero. Calls that overlap on one GPU (concurrent streams, or
+ * graphs replayed concurrently) race on the array: order them. */
+#define HATTN_DECODE_STATIC_SCRATCH_BYTES (6u << 20)
+int hattn_decode_static(const hattn_layer_desc* desc, const void* q,
+                        const void* k, const void* v, const void* gate,
+                        int32_t batch, const int32_t* pos, int32_t max_pos,
+                        const hattn_kv_cache* cache, void* out,
+                        hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * The attention block around the core (page §2 figure 1, the decoder
  * layer's dataflow; §1 config table; §3; §5): with x the block input,

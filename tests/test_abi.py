@@ -292,3 +292,22 @@ def test_decode_workspace_size_covers_every_position(L, layer, kind, cap, B, Hq,
             continue
         st = _decode(L, d, c, B=B, max_pos=mp, ws_bytes=ws)
         assert st in (0, -10), (mp, st)
+
+
+@fake_pointers
+def test_decode_static_validates_before_using_its_scratch(L):
+    """hattn_decode_static checks its arguments like hattn_decode before it
+    looks up the static array (here the valid call then fails at the launch,
+    without a GPU)."""
+    fu = hb.layer_desc("full")
+    def st(desc, cache, B=1, max_pos=10, pos=FAKE):
+        return L.hattn_decode_static(ctypes.byref(desc), FAKE, FAKE, FAKE, FAKE, B, pos, max_pos,
+                                     ctypes.byref(cache), FAKE, None)
+    lin = hb.KvCacheC(FAKE, FAKE, hb.KV_LINEAR, 1, 1 << 20)
+    g2 = hb.layer_desc("full", 8, 2)
+    g2.num_kv_heads = 4
+    assert st(g2, lin) == -3
+    assert st(fu, hb.KvCacheC(FAKE, FAKE, hb.KV_LINEAR, 2, 4096)) == -6
+    assert st(fu, lin, max_pos=1 << 20) == -7
+    assert st(fu, lin, pos=0) == -1
+    assert st(fu, lin, max_pos=(1 << 20) - 1) == -10      # valid: reaches the launch
