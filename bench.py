@@ -161,88 +161,80 @@ def to_paged(torch, hb, ck, cv, page, seed):
     return hb.KVCache.paged(pool(ck), pool(cv), perm.view(B, n).to(torch.int32).to(ck.device))
 
 
-class ClockSampler:
-    """Samples the GPU's shader clock from the driver's hwmon node
-    (freq1_input, Hz) on a background thread while a timed region runs.
-    Reports the mean and range of the samples, or why none were taken."""
+class ClockStamps:
+    """Counter rates over a region of the current stream: the library's stamp
+    kernel records, per block, the s_memtime and s_memrealtime counters before
+    and after the region, and events time it. Reports each counter's rate
+    (MHz of the region's event time); the shader clock is the s_memtime rate
+    where that counter follows the shader clock."""
 
-    def __init__(self, torch, dev, period_s=0.002):
-        import glob
-        import threading
-
-        self.period = period_s
-        self.samples = []
-        self.path = None
-        self.reason = None
-        self._stop = threading.Event()
-        self._thread = None
-        try:
-            props = torch.cuda.get_device_properties(dev)
-            bus = "%02x:%02x" % (props.pci_bus_id, props.pci_device_id)
-            for card in sorted(glob.glob("/sys/class/drm/card*/device")):
-                real = os.path.realpath(card)
-                if os.path.basename(real).split(":", 1)[-1].startswith(bus):
-                    hw = sorted(glob.glob(os.path.join(card, "hwmon", "hwmon*", "freq1_input")))
-                    if hw:
-                        self.path = hw[0]
-                    break
-            if self.path is None:
-                self.reason = f"no hwmon freq1_input for PCI bus {bus}"
-        except Exception as e:  # the sampler is optional: report why it is off
-            self.reason = f"{type(e).__name__}: {e}"
-
-    def _run(self):
-        while not self._stop.is_set():
-            try:
-                with open(self.path) as f:
-                    self.samples.append(int(f.read().strip()) / 1e9)
-            except (OSError, ValueError) as e:
-                self.reason = f"{type(e).__name__}: {e}"
-                return
-            self._stop.wait(self.period)
+    def __init__(self, torch, hb, dev, blocks=8):
+        self.torch, self.hb = torch, hb
+        self.s0 = torch.zeros((blocks, 2), dtype=torch.int64, device=dev)
+        self.s1 = torch.zeros_like(self.s0)
+        self.e0 = torch.cuda.Event(enable_timing=True)
+        self.e1 = torch.cuda.Event(enable_timing=True)
 
     def __enter__(self):
-        import threading
-
-        if self.path:
-            self._thread = threading.Thread(target=self._run, daemon=True)
-            self._thread.start()
+        self.hb.debug_clock_stamp(self.s0, self.s0.shape[0])
+        self.e0.record()
         return self
 
     def __exit__(self, *exc):
-        self._stop.set()
-        if self._thread:
-            self._thread.join()
+        self.e1.record()
+        self.hb.debug_clock_stamp(self.s1, self.s1.shape[0])
 
-    def summary(self):
-        if not self.samples:
-            return {"avg_GHz": None, "reason": self.reason or "no samples"}
-        x = self.samples
-        return {"avg_GHz": round(sum(x) / len(x), 3), "min_GHz": round(min(x), 3), "max_GHz": round(max(x), 3),
-                "samples": len(x), "source": self.path}
+    def rates(self):
+        self.torch.cuda.synchronize()
+        ms = self.e0.elapsed_time(self.e1)
+        a, b = self.s0.cpu(), self.s1.cpu()
+        n = a.shape[0]
+        mt = sum(int(b[i, 0]) - int(a[i, 0]) for i in range(n)) / n
+        rt = sum(int(b[i, 1]) - int(a[i, 1]) for i in range(n)) / n
+        return {"region_ms": round(ms, 4), "memtime_MHz": round(mt / (ms * 1e3), 1),
+                "memrealtime_MHz": round(rt / (ms * 1e3), 1)}
 
 
-def ceilings(torch, dev, steps=5):
-    """What plain vendor kernels reach on this GPU, timed beside the path:
-    torch.sum over 4 GiB of bf16 (a pure read), the same over 8 distinct
-    128 MiB buffers in turn (the sliding decode's size), and a bf16 GEMM of
-    8192^3 (hipBLASLt). Event-timed, back to back."""
+def ceilings(torch, hb, dev, steps=5):
+    """What the chip itself delivers, timed beside the path (event-timed,
+    back to back): the library's plain streaming-read probe over 4 GiB and
+    over 8 distinct 128 MiB buffers in turn (the sliding decode's size and
+    grid), back-to-back bf16 MFMA on every CU (with the shader clock over
+    it), and torch's bf16 GEMM of 8192^3 (hipBLASLt)."""
     res = {}
-    n4 = 1 << 31  # 4 GiB of bf16
-    big = torch.empty(n4, dtype=torch.bfloat16, device=dev).normal_()
-    ms = time_calls(torch, lambda: big.sum(dtype=torch.float32), steps, 2)
-    res["read_4GiB_torch_sum"] = {"ms": round(ms, 4), "GB_per_s": round(2 * n4 / (ms * 1e-3) / 1e9, 1)}
+    sink = torch.zeros(8192, dtype=torch.int32, device=dev)
+    big = torch.empty(1 << 30, dtype=torch.int32, device=dev).random_()  # 4 GiB
+    sweep = []
+    for blocks in (256, 512, 1024, 2048, 4096):
+        ms = time_calls(torch, lambda: hb.debug_read_probe(big, blocks, sink), steps, 2)
+        sweep.append({"blocks": blocks, "ms": round(ms, 4), "GB_per_s": round(4 * big.numel() / (ms * 1e-3) / 1e9, 1)})
+    res["read_4GiB_probe"] = max(sweep, key=lambda r: r["GB_per_s"])
+    res["read_4GiB_probe_sweep"] = sweep
     del big
-    sets = [torch.empty(1 << 26, dtype=torch.bfloat16, device=dev).normal_() for _ in range(8)]
-    it = [0]
+    sets = [torch.empty(1 << 25, dtype=torch.int32, device=dev).random_() for _ in range(8)]  # 8 x 128 MiB
+    for blocks in (256, 1024):
+        it = [0]
 
-    def rd():
-        sets[it[0] % 8].sum(dtype=torch.float32)
-        it[0] += 1
+        def rd():
+            hb.debug_read_probe(sets[it[0] % 8], blocks, sink)
+            it[0] += 1
 
-    ms = time_calls(torch, rd, 8 * steps, 8)
-    res["read_8x128MiB_torch_sum"] = {"us": round(ms * 1e3, 2), "GB_per_s": round((1 << 27) / (ms * 1e-3) / 1e9, 1)}
+        ms = time_calls(torch, rd, 8 * steps, 8)
+        res[f"read_8x128MiB_probe_{blocks}_blocks"] = {"us": round(ms * 1e3, 2),
+                                                      "GB_per_s": round((1 << 27) / (ms * 1e-3) / 1e9, 1)}
     del sets
+    fsink = torch.zeros(256 * 4, dtype=torch.float32, device=dev)
+    iters = 8000
+    hb.debug_mfma_probe(256, iters, fsink)
+    with ClockStamps(torch, hb, dev) as clk:
+        ms = time_calls(torch, lambda: hb.debug_mfma_probe(256, iters, fsink), steps, 1)
+    fl = 256 * 4 * iters * 8 * 32768
+    tf = fl / (ms * 1e-3) / 1e12
+    # one 32x32x16 MFMA per 32 cycles per SIMD at full issue: the clock the
+    # rate implies (1,024 SIMDs x 1,024 flop per cycle)
+    res["mfma_bf16_32x32x16_probe"] = {"ms": round(ms, 4), "TFLOP_per_s": round(tf, 1),
+                                       "implied_sclk_GHz": round(tf * 1e12 / (1024 * 1024) / 1e9, 3),
+                                       "counters": clk.rates()}
     a = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
     b = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
     ms = time_calls(torch, lambda: torch.mm(a, b), steps, 2)
@@ -464,7 +456,7 @@ def run(args):
     torch.cuda.synchronize()
     hb.hattn_profile_read(hb.PROFILE_PREFILL)
     hb.hattn_profile_enable(True)
-    with ClockSampler(torch, dev) as clk:
+    with ClockStamps(torch, hb, dev) as clk:
         ms = time_calls(torch, prefill, args.steps, 0)
     hb.hattn_profile_enable(False)
     n, attn_total = hb.hattn_profile_read(hb.PROFILE_PREFILL)
@@ -478,7 +470,7 @@ def run(args):
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
         "traffic": counter_traffic("prefill_full_s8192"),
         "kernel": "prefill_attn_kernel", "flop_per_launch": flops, "avg_launch_ms": round(attn_ms, 5),
-        "launches_timed": n, "sclk_during_timed_steps": clk.summary(),
+        "launches_timed": n, "counters_during_timed_steps": clk.rates(),
     }
     del inp, cache, out, ws
     torch.cuda.empty_cache()
@@ -617,7 +609,7 @@ def run(args):
         del pg
         torch.cuda.empty_cache()
 
-    ceil = None if args.skip_ceilings else ceilings(torch, dev)
+    ceil = None if args.skip_ceilings else ceilings(torch, hb, dev)
     if ceil:
         log(f"ceilings: {json.dumps(ceil)}")
 
@@ -660,9 +652,9 @@ def main(argv=None):
                     help="skip the sliding 1024-token and 1.7B chunked prefill timings")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-ceilings", action="store_true",
-                    help="skip the plain torch read and GEMM timings")
+                    help="skip the read / MFMA probe and GEMM timings")
     ap.add_argument("--ceilings", action="store_true",
-                    help="only time the plain torch reads and GEMM (for kernel traces)")
+                    help="only time the read / MFMA probes and the GEMM (for kernel traces)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the copy of known size used to scale HBM counters")
     ap.add_argument("--block-only", action="store_true",
@@ -679,7 +671,8 @@ def main(argv=None):
         line = copy_calibration()
     elif args.ceilings:
         import torch
-        line = ceilings(torch, torch.device("cuda:0"), steps=max(args.steps, 5))
+        from full_gqa_attention_spark2_amd import binding as hb
+        line = ceilings(torch, hb, torch.device("cuda:0"), steps=max(args.steps, 5))
     elif args.block_only:
         import torch
         from full_gqa_attention_spark2_amd import binding as hb, synth

@@ -634,6 +634,28 @@ int hattn_profile_read(int kind, int64_t* count, double* total_ms) {
   return st;
 }
 
+int hattn_debug_clock_stamp(uint64_t* out, int32_t blocks, hipStream_t stream) {
+  if (blocks < 1 || blocks > 1024) return HATTN_ERR_SHAPE;
+  if (!out) return HATTN_ERR_NULL;
+  if ((uintptr_t)out & 7u) return HATTN_ERR_ALIGN;
+  return from_hip(launch_clock_stamp((unsigned long long*)out, blocks, stream));
+}
+
+int hattn_debug_read_probe(const void* buf, size_t bytes, int32_t blocks, uint32_t* sink, hipStream_t stream) {
+  if (blocks < 1 || bytes % 16) return HATTN_ERR_SHAPE;
+  if (bytes == 0) return HATTN_OK;
+  if (!buf || !sink) return HATTN_ERR_NULL;
+  if (!aligned16(buf) || ((uintptr_t)sink & 3u)) return HATTN_ERR_ALIGN;
+  return from_hip(launch_read_probe(buf, bytes, blocks, sink, stream));
+}
+
+int hattn_debug_mfma_probe(int32_t blocks, int32_t iters, float* sink, hipStream_t stream) {
+  if (blocks < 1 || iters < 1) return HATTN_ERR_SHAPE;
+  if (!sink) return HATTN_ERR_NULL;
+  if ((uintptr_t)sink & 3u) return HATTN_ERR_ALIGN;
+  return from_hip(launch_mfma_probe(blocks, iters, sink, stream));
+}
+
 int hattn_debug_index_probe(const hattn_layer_desc* desc, int32_t kv_kind, int32_t capacity,
                             int32_t q_pos0, int32_t n_q, uint8_t* mask, int32_t* key_pos,
                             int32_t* slot, hipStream_t stream) {

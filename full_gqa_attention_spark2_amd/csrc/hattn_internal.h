@@ -180,6 +180,9 @@ hipError_t decode_static_scratch(void** ptr);
 hipError_t launch_rope_apply(const RopeApplyArgs& a, hipStream_t s);
 hipError_t launch_index_probe(const ProbeArgs& a, hipStream_t s);
 hipError_t launch_rms_norm(const RmsNormArgs& a, hipStream_t s);
+hipError_t launch_clock_stamp(unsigned long long* out, int blocks, hipStream_t s);
+hipError_t launch_read_probe(const void* buf, size_t bytes, int blocks, uint32_t* sink, hipStream_t s);
+hipError_t launch_mfma_probe(int blocks, int iters, float* sink, hipStream_t s);
 hipError_t launch_residual_add(const uint16_t* x, const uint16_t* y, uint16_t* out, long long n, hipStream_t s);
 
 }  // namespace hattn

@@ -1,0 +1,95 @@
+// Measurement probes: what the chip itself delivers, measured beside the
+// attention kernels so that their roofline fractions can be read against it.
+//   - clock_stamp_kernel: the shader clock counter and the constant 100 MHz
+//     reference counter, one pair per block, so that two stamps around a
+//     timed region give the average shader clock over it;
+//   - read_probe_kernel: a plain streaming read (16 B per lane, eight loads in
+//     flight per thread), the practical HBM read rate at a given size;
+//   - mfma_probe_kernel: back-to-back bf16 MFMA 32x32x16 on pseudo-random
+//     operands, the practical matrix-core rate under full load (the clock
+//     drops under it).
+// None of them is on the attention path.
+#include "hattn_device.h"
+#include "hattn_internal.h"
+
+namespace hattn {
+
+namespace {
+
+__global__ void clock_stamp_kernel(unsigned long long* out) {
+  if (threadIdx.x == 0) {
+    const unsigned long long t = __builtin_amdgcn_s_memtime();
+    const unsigned long long r = __builtin_amdgcn_s_memrealtime();
+    out[2 * blockIdx.x] = t;
+    out[2 * blockIdx.x + 1] = r;
+  }
+}
+
+// Block b streams its contiguous share of the buffer; every thread keeps
+// eight 16-byte loads in flight and folds them into one word.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* buf, size_t n16, uint32_t* sink) {
+  const size_t per_block = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t lo = (size_t)blockIdx.x * per_block;
+  const size_t hi = min(lo + per_block, n16);
+  uint32_t x = 0;
+  size_t i = lo + threadIdx.x;
+  for (; i + 7 * 256 < hi; i += 8 * 256) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * 256);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < hi; i += 256) {
+    const u32x4 v = buf[i];
+    x ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  // a data-dependent store keeps the loads alive (random data never hits it)
+  if (x == 0x9e3779b9u) sink[blockIdx.x] = x;
+}
+
+// Four waves per block (one per SIMD when one block runs per CU); each wave
+// chains `iters` rounds of 8 independent 32x32x16 MFMAs.
+__global__ __launch_bounds__(256, 1) void mfma_probe_kernel(int iters, float* sink) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+  uint32_t s = (blockIdx.x * 256 + threadIdx.x) * 2654435761u + 12345u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    s = s * 1664525u + 1013904223u;
+    a[j] = (__bf16)((float)(s >> 16) * (1.0f / 32768.0f) - 1.0f);
+    s = s * 1664525u + 1013904223u;
+    b[j] = (__bf16)((float)(s >> 16) * (1.0f / 32768.0f) - 1.0f);
+  }
+  f32x16 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = f32x16{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
+  }
+  float x = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x += acc[i][lane & 15];
+  if (lane == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = x;
+}
+
+}  // namespace
+
+hipError_t launch_clock_stamp(unsigned long long* out, int blocks, hipStream_t s) {
+  hipLaunchKernelGGL(clock_stamp_kernel, dim3(blocks), dim3(64), 0, s, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_read_probe(const void* buf, size_t bytes, int blocks, uint32_t* sink, hipStream_t s) {
+  hipLaunchKernelGGL(read_probe_kernel, dim3(blocks), dim3(256), 0, s, (const u32x4*)buf, bytes / 16, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma_probe(int blocks, int iters, float* sink, hipStream_t s) {
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3(blocks), dim3(256), 0, s, iters, sink);
+  return hipGetLastError();
+}
+
+}  // namespace hattn
