@@ -386,15 +386,15 @@ def block_decode_workspace_size(desc, weights, cache, B):
 
 
 def hattn_block_prefill(desc, weights, x, cu_seqlens, start_pos, cache, out=None, workspace=None):
-    """The attention block over packed new tokens x [T, hidden] (host
-    cu_seqlens [B+1], start positions [B]); returns out [T, hidden] =
-    x + out_proj(core(...)); out may be x."""
+    """The attention block over packed new tokens x [T, hidden] (fp32, the
+    residual stream; host cu_seqlens [B+1], start positions [B]); returns
+    out [T, hidden] fp32 = x + out_proj(core(...)); out may be x."""
     T, H = x.shape
     B = len(cu_seqlens) - 1
-    _need(x, "x", shape=(T, weights.hidden))
+    _need(x, "x", torch.float32, (T, weights.hidden))
     if out is None:
         out = torch.empty_like(x)
-    _need(out, "out", shape=x.shape)
+    _need(out, "out", torch.float32, x.shape)
     cu = (ctypes.c_int32 * (B + 1))(*[int(v) for v in cu_seqlens])
     sp = (ctypes.c_int32 * B)(*[int(v) for v in start_pos])
     cc, wc = cache.c(), weights.c()
@@ -407,14 +407,15 @@ def hattn_block_prefill(desc, weights, x, cu_seqlens, start_pos, cache, out=None
 
 
 def hattn_block_decode(desc, weights, x, pos, max_pos, cache, out=None, workspace=None):
-    """The attention block for one token per sequence, x [B, hidden], at
-    device int32 positions pos [B]; returns out [B, hidden]; out may be x."""
+    """The attention block for one token per sequence, x [B, hidden] fp32,
+    at device int32 positions pos [B]; returns out [B, hidden] fp32; out
+    may be x."""
     B, H = x.shape
-    _need(x, "x", shape=(B, weights.hidden))
+    _need(x, "x", torch.float32, (B, weights.hidden))
     _need(pos, "pos", torch.int32, (B,))
     if out is None:
         out = torch.empty_like(x)
-    _need(out, "out", shape=x.shape)
+    _need(out, "out", torch.float32, x.shape)
     cc, wc = cache.c(), weights.c()
     ws = _workspace(block_decode_workspace_size(desc, weights, cache, B), x.device, workspace)
     _check("hattn_block_decode", lib().hattn_block_decode(

@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhattn.so")
 SOURCES = ["hattn_api.cpp", "hattn_plan.cpp", "hattn_block.cpp", "hattn_rope.hip", "hattn_prefill.hip",
-           "hattn_decode.hip", "hattn_norm.hip", "hattn_probe.hip"]
+           "hattn_decode.hip", "hattn_norm.hip", "hattn_probe.hip", "hattn_gemm.hip"]
 ARCH = "gfx950"
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",

@@ -1,8 +1,9 @@
 // The attention block around the core (page "Spark-X2.5 架构（4B / 1.7B）",
 // §2 figure 1: RMSNorm -> q_k_v_proj and g_proj -> RoPE and attention ->
-// per-head gate -> out_proj -> + residual). The two projections are plain
-// GEMMs and run on hipBLASLt; the norm, the core and the residual add are
-// this library's kernels.
+// per-head gate -> out_proj -> + residual; §5: the residual stream is fp32).
+// The two projections are plain GEMMs: hipBLASLt for many tokens, this
+// library's weight-streaming kernel for a few (decode); the norm, the core
+// and the residual add are this library's kernels.
 #include <stdint.h>
 
 #include <algorithm>
@@ -130,6 +131,11 @@ void tune(hipblasLtHandle_t h, GemmPlan* p, const void* W, const void* A, void* 
 int gemm(const void* W, int N, int K, const void* A, int T, long long lda, void* D, long long ldd, void* ws,
          hipStream_t s) {
   if (T == 0) return HATTN_OK;
+  // a few tokens (decode): the weight-streaming kernel of this library
+  if (skinny_gemm_fits(N, K, T, lda, ldd, W, A, D)) {
+    SkinnyGemmArgs g{(const uint16_t*)W, (const uint16_t*)A, (uint16_t*)D, N, K, T, lda, ldd};
+    return launch_skinny_gemm(g, s) == hipSuccess ? HATTN_OK : HATTN_ERR_LAUNCH;
+  }
   hipblasLtHandle_t h = lt_handle();
   if (!h) return HATTN_ERR_LAUNCH;
   GemmPlan* p = gemm_plan(h, N, K, T, lda, ldd);
@@ -184,7 +190,7 @@ int block_run(const hattn_layer_desc* desc, const hattn_block_weights* w, const 
   uint16_t* attn = (uint16_t*)(ws + L.attn);
   uint16_t* y = (uint16_t*)(ws + L.y);
   RmsNormArgs na{};
-  na.x = (const uint16_t*)x;
+  na.x = (const float*)x;
   na.w = (const uint16_t*)w->norm_weight;
   na.y = h;
   na.T = (int)T;
@@ -198,8 +204,8 @@ int block_run(const hattn_layer_desc* desc, const hattn_block_weights* w, const 
   if (st != HATTN_OK) return st;
   st = gemm(w->o_weight, H, Hq * 256, attn, (int)T, (long long)Hq * 256, y, H, ws + L.gemm, s);
   if (st != HATTN_OK) return st;
-  return launch_residual_add((const uint16_t*)x, y, (uint16_t*)out, T * H, s) == hipSuccess ? HATTN_OK
-                                                                                           : HATTN_ERR_LAUNCH;
+  return launch_residual_add((const float*)x, y, (float*)out, T * H, s) == hipSuccess ? HATTN_OK
+                                                                                     : HATTN_ERR_LAUNCH;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }

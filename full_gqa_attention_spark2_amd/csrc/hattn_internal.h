@@ -123,13 +123,24 @@ struct ProbeArgs {
   int ring, cap, window, q_pos0, n_q;
 };
 
-// Input RMSNorm of the attention block: y[t] = bf16(w * x[t] / rms(x[t])).
+// Input RMSNorm of the attention block: y[t] = bf16(w * x[t] / rms(x[t]))
+// from the fp32 residual stream x.
 struct RmsNormArgs {
-  const uint16_t* x;  // bf16 [T][H]
+  const float* x;     // fp32 [T][H]
   const uint16_t* w;  // bf16 [H]
   uint16_t* y;        // bf16 [T][H]
   int T, H;           // H a multiple of 8
   float eps;
+};
+
+// Skinny GEMM of the attention block's decode projections:
+// d[T][N] = a[T][K] . w[N][K]^T, bf16, fp32 accumulation, T <= 64.
+struct SkinnyGemmArgs {
+  const uint16_t* w;  // [N][K]
+  const uint16_t* a;  // [T] rows lda elements apart
+  uint16_t* d;        // [T] rows ldd elements apart
+  int N, K, T;
+  long long lda, ldd;
 };
 
 // Kernel arguments travel by value; keep each struct within 4 KiB.
@@ -180,9 +191,14 @@ hipError_t decode_static_scratch(void** ptr);
 hipError_t launch_rope_apply(const RopeApplyArgs& a, hipStream_t s);
 hipError_t launch_index_probe(const ProbeArgs& a, hipStream_t s);
 hipError_t launch_rms_norm(const RmsNormArgs& a, hipStream_t s);
+// Whether the skinny GEMM takes a shape (T <= 64, K a multiple of 512, N,
+// lda, ldd multiples of 8, 16-byte aligned pointers), and its launch.
+bool skinny_gemm_fits(int N, int K, int T, long long lda, long long ldd, const void* w, const void* a,
+                      const void* d);
+hipError_t launch_skinny_gemm(const SkinnyGemmArgs& g, hipStream_t s);
 hipError_t launch_clock_stamp(unsigned long long* out, int blocks, hipStream_t s);
 hipError_t launch_read_probe(const void* buf, size_t bytes, int blocks, uint32_t* sink, hipStream_t s);
 hipError_t launch_mfma_probe(int blocks, int iters, float* sink, hipStream_t s);
-hipError_t launch_residual_add(const uint16_t* x, const uint16_t* y, uint16_t* out, long long n, hipStream_t s);
+hipError_t launch_residual_add(const float* x, const uint16_t* y, float* out, long long n, hipStream_t s);
 
 }  // namespace hattn

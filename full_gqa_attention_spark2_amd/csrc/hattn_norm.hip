@@ -1,7 +1,9 @@
 // Elementwise kernels of the attention block around the core (page
-// "Spark-X2.5 架构（4B / 1.7B）", §2 figure 1 decoder-layer dataflow and §5
-// norms): the input RMSNorm and the residual add. Both are HBM-bound; each
-// thread moves 16-byte chunks (8 bf16 values).
+// "Spark-X2.5 架构（4B / 1.7B）", §2 figure 1 decoder-layer dataflow and §5:
+// the input embedding is taken to fp32 for the backbone, so the residual
+// stream x is fp32; the norm computes in fp32 and hands the projections the
+// model dtype, bf16): the input RMSNorm and the residual add. Both are
+// HBM-bound; each thread moves 8 values at a time.
 #include <algorithm>
 
 #include "hattn_device.h"
@@ -22,6 +24,12 @@ __device__ __forceinline__ void unpack8f(uint4 u, float* x) {
   }
 }
 
+__device__ __forceinline__ void load8f32(const float* p, float* x) {
+  const float4 a = ((const float4*)p)[0], b = ((const float4*)p)[1];
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
 __device__ __forceinline__ uint4 pack8f(const float* x) {
   uint32_t w[4];
 #pragma unroll
@@ -32,20 +40,20 @@ __device__ __forceinline__ uint4 pack8f(const float* x) {
 
 }  // namespace
 
-// One block per token: y = bf16(w * x / sqrt(mean(x^2) + eps)), in fp32
-// (page §5: the norm is computed in fp32, multiplied by the weight, and cast
-// back to the model dtype).
+// One block per token: y = bf16(w * x / sqrt(mean(x^2) + eps)) from the
+// fp32 residual stream x, computed in fp32 (page §5: the norm is computed in
+// fp32, multiplied by the weight, and cast back to the model dtype).
 __global__ __launch_bounds__(kNormThreads) void rms_norm_kernel(RmsNormArgs a) {
   __shared__ float part[kNormThreads / 64];
   const int t = threadIdx.x;
-  const uint4* x = (const uint4*)(a.x + (size_t)blockIdx.x * a.H);
+  const float* x = a.x + (size_t)blockIdx.x * a.H;
   uint4* y = (uint4*)(a.y + (size_t)blockIdx.x * a.H);
   const uint4* w = (const uint4*)a.w;
   const int n = a.H / 8;
   float ss = 0.f;
   for (int c = t; c < n; c += kNormThreads) {
     float v[8];
-    unpack8f(x[c], v);
+    load8f32(x + 8 * c, v);
 #pragma unroll
     for (int j = 0; j < 8; ++j) ss = fmaf(v[j], v[j], ss);
   }
@@ -58,7 +66,7 @@ __global__ __launch_bounds__(kNormThreads) void rms_norm_kernel(RmsNormArgs a) {
   const float r = rsqrtf(tot / (float)a.H + a.eps);
   for (int c = t; c < n; c += kNormThreads) {
     float v[8], g[8];
-    unpack8f(x[c], v);
+    load8f32(x + 8 * c, v);
     unpack8f(w[c], g);
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = v[j] * r * g[j];
@@ -66,17 +74,18 @@ __global__ __launch_bounds__(kNormThreads) void rms_norm_kernel(RmsNormArgs a) {
   }
 }
 
-// out = bf16(x + y) over n8 chunks of 8 values (the residual add of the
-// block; out may be x).
-__global__ __launch_bounds__(256) void residual_add_kernel(const uint16_t* x, const uint16_t* y, uint16_t* out,
+// out = x + y in fp32 over n8 chunks of 8 values: the residual add of the
+// block, the fp32 stream x plus the bf16 out_proj result y (out may be x).
+__global__ __launch_bounds__(256) void residual_add_kernel(const float* x, const uint16_t* y, float* out,
                                                            long long n8) {
   for (long long c = (long long)blockIdx.x * 256 + threadIdx.x; c < n8; c += (long long)gridDim.x * 256) {
     float a[8], b[8];
-    unpack8f(((const uint4*)x)[c], a);
+    load8f32(x + 8 * c, a);
     unpack8f(((const uint4*)y)[c], b);
 #pragma unroll
     for (int j = 0; j < 8; ++j) a[j] += b[j];
-    ((uint4*)out)[c] = pack8f(a);
+    ((float4*)(out + 8 * c))[0] = make_float4(a[0], a[1], a[2], a[3]);
+    ((float4*)(out + 8 * c))[1] = make_float4(a[4], a[5], a[6], a[7]);
   }
 }
 
@@ -86,7 +95,7 @@ hipError_t launch_rms_norm(const RmsNormArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_residual_add(const uint16_t* x, const uint16_t* y, uint16_t* out, long long n, hipStream_t s) {
+hipError_t launch_residual_add(const float* x, const uint16_t* y, float* out, long long n, hipStream_t s) {
   const long long n8 = n / 8;
   if (n8 == 0) return hipSuccess;
   const long long blocks = std::min<long long>((n8 + 255) / 256, 4096);

@@ -111,5 +111,5 @@ def block_weights(hidden, Hq, Hkv, D=256, seed=0):
 
 
 def hidden_states(T, hidden, seed=0):
-    """Block inputs x [T, hidden] ~ N(0, 1), bf16."""
-    return _normal(_gen(seed), (T, hidden))
+    """Block inputs x [T, hidden] ~ N(0, 1), fp32 (the residual stream)."""
+    return torch.randn((T, hidden), generator=_gen(seed), dtype=torch.float32)

@@ -237,18 +237,21 @@ int hattn_decode_static(const hattn_layer_desc* desc, const void* q,
 
 /* ------------------------------------------------------------------------
  * The attention block around the core (page §2 figure 1, the decoder
- * layer's dataflow; §1 config table; §3; §5): with x the block input,
+ * layer's dataflow; §1 config table; §3; §5): with x the block input, the
+ * fp32 residual stream (§5: the input embedding is taken to fp32 for the
+ * backbone),
  *   h = RMSNorm(x)                     fp32, times the weight, cast to bf16
  *   [q | k | v | g] = h W_qkvg^T       q_k_v_proj and g_proj, bf16 outputs
  *   a = attention core(q, k, v, g)     as hattn_prefill_varlen / hattn_decode
  *   out = x + a W_o^T                  out_proj (bf16), then the residual add
- *                                      in fp32 with one bf16 rounding
- * Linear layers have no bias (page §5: attention_bias false). The GEMMs run
- * on hipBLASLt (bf16 in and out, fp32 accumulate) through one handle per
- * device, created on first use; the other steps are this library's kernels.
- * The first call of a GEMM shape outside stream capture times a few
- * hipBLASLt candidates on its own buffers and waits for them (once per
- * shape and process); later calls, and calls under capture, do not wait.
+ *                                      in fp32 (out stays fp32)
+ * Linear layers have no bias (page §5: attention_bias false). The GEMMs are
+ * bf16 in and out with fp32 accumulation: for at most 64 tokens (decode
+ * batches) this library's weight-streaming kernel, otherwise hipBLASLt
+ * through one handle per device, created on first use. The first hipBLASLt
+ * call of a GEMM shape outside stream capture times a few candidates on its
+ * own buffers and waits for them (once per shape and process); later calls,
+ * and calls under capture, do not wait.
  */
 typedef struct {
   const void* norm_weight;  /* bf16 [hidden]: the input RMSNorm's weight    */
@@ -262,8 +265,8 @@ typedef struct {
 } hattn_block_weights;
 
 /* Prefill of the block over a ragged batch, layouts as hattn_prefill_varlen:
- *   x:   bf16 [T][hidden] block inputs of the packed new tokens
- *   out: bf16 [T][hidden]; may be x (the residual stream updated in place)
+ *   x:   fp32 [T][hidden] block inputs of the packed new tokens
+ *   out: fp32 [T][hidden]; may be x (the residual stream updated in place)
  * The rotated keys and the values go to the cache as in hattn_prefill.
  * Errors: as hattn_prefill_varlen, plus HATTN_ERR_SHAPE for a hidden size
  * that is not a positive multiple of 8 or rms_eps <= 0, HATTN_ERR_NULL for
@@ -280,7 +283,7 @@ int hattn_block_prefill(const hattn_layer_desc* desc,
                         void* out, void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
 
-/* Decode of the block: x, out bf16 [B][hidden] (out may be x); pos,
+/* Decode of the block: x, out fp32 [B][hidden] (out may be x); pos,
  * max_pos and the cache as in hattn_decode. Errors as hattn_decode plus
  * those of hattn_block_prefill's weights. */
 size_t hattn_block_decode_workspace_size(const hattn_layer_desc* desc,

@@ -420,9 +420,11 @@ def block_prefill_ref(x, norm_w, w_qkvg, w_o, eps, cu_seqlens, start_pos, *, Hq,
                       hist_v=None, hist_pos=None):
     """One attention block over a ragged batch of new tokens x [T, hidden]
     ([SPARK] figure 1): RMSNorm -> fused q/k/v/g projection -> the core
-    (prefill_varlen_ref) -> out_proj -> + residual. Tensors between modules
-    are bf16 (the model dtype; the core's output is cast back as [SPARK §3]
-    states); the returned sum x + out_proj(...) is left unrounded.
+    (prefill_varlen_ref) -> out_proj -> + residual. x is the residual
+    stream, which [SPARK §5] keeps in fp32 (the input embedding is taken to
+    fp32 for the backbone); module outputs are bf16 (the model dtype; the
+    core's output is cast back as [SPARK §3] states); the returned sum
+    x + out_proj(...) is left unrounded.
     Returns (out [T, hidden] fp64, k_hat [T, Hkv, D])."""
     h = rms_norm(x, norm_w, eps)
     q, k, v, g = split_qkvg(linear_bf16(h, w_qkvg), Hq, Hkv)
