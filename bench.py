@@ -507,6 +507,7 @@ def run(args):
         prefill_configs["sliding_s1024"] = {
             "us_per_call": {k: round(v * 1e3, 2) for k, v in t.items()}, "flop_per_call": fl,
             "TFLOP_per_s": round(tf, 2), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    if prefill_configs is not None and not args.skip_chunked:
         # 1.7B shape: 8 / 2 heads, batch 2, a 4096-token chunk at 262144:
         # the 28-layer pass measured as a whole, and each layer type alone
         s0, S5 = 262144, 4096
@@ -543,6 +544,7 @@ def run(args):
             "full_layer_ms": {k: round(v, 4) for k, v in tfu.items()}, "full_layer_flop": flf,
             "full_layer_TFLOP_per_s": round(flf / (tfu["median"] * 1e-3) / 1e12, 2)}
 
+    if prefill_configs is not None and not args.skip_block:
         prefill_configs["block_4b"] = block_bench(torch, hb, synth, dev, args)
 
     # ---------------------------------------------------------------- decode
@@ -651,6 +653,9 @@ def main(argv=None):
     ap.add_argument("--skip-prefill-configs", action="store_true",
                     help="skip the sliding 1024-token and 1.7B chunked prefill timings")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-chunked", action="store_true",
+                    help="skip the 1.7B chunked prefill timings (28-layer pass, per layer type, paged)")
+    ap.add_argument("--skip-block", action="store_true", help="skip the attention-block timings")
     ap.add_argument("--skip-ceilings", action="store_true",
                     help="skip the read / MFMA probe and GEMM timings")
     ap.add_argument("--ceilings", action="store_true",
