@@ -128,12 +128,17 @@ void tune(hipblasLtHandle_t h, GemmPlan* p, const void* W, const void* A, void* 
   p->tuned = true;
 }
 
+// D = A . W^T. With resid_out set and the weight-streaming kernel taken,
+// the residual add is fused into its epilogue (resid_out = resid_x +
+// bf16(D) in fp32, rows ldd apart; D is not written) and *fused is set.
 int gemm(const void* W, int N, int K, const void* A, int T, long long lda, void* D, long long ldd, void* ws,
-         hipStream_t s) {
+         hipStream_t s, const float* resid_x = nullptr, float* resid_out = nullptr, bool* fused = nullptr) {
   if (T == 0) return HATTN_OK;
   // a few tokens (decode): the weight-streaming kernel of this library
-  if (skinny_gemm_fits(N, K, T, lda, ldd, W, A, D)) {
-    SkinnyGemmArgs g{(const uint16_t*)W, (const uint16_t*)A, (uint16_t*)D, N, K, T, lda, ldd};
+  if (skinny_gemm_fits(N, K, T, lda, ldd, W, A, D) &&
+      (!resid_out || ((((uintptr_t)resid_x | (uintptr_t)resid_out) & 15u) == 0))) {
+    SkinnyGemmArgs g{(const uint16_t*)W, (const uint16_t*)A, (uint16_t*)D, N, K, T, lda, ldd, resid_x, resid_out};
+    if (fused) *fused = resid_out != nullptr;
     return launch_skinny_gemm(g, s) == hipSuccess ? HATTN_OK : HATTN_ERR_LAUNCH;
   }
   hipblasLtHandle_t h = lt_handle();
@@ -202,8 +207,10 @@ int block_run(const hattn_layer_desc* desc, const hattn_block_weights* w, const 
   st = core(qkvg, qkvg + (size_t)Hq * 256, qkvg + (size_t)(Hq + Hkv) * 256, qkvg + (size_t)(Hq + 2 * Hkv) * 256,
             n1, attn);
   if (st != HATTN_OK) return st;
-  st = gemm(w->o_weight, H, Hq * 256, attn, (int)T, (long long)Hq * 256, y, H, ws + L.gemm, s);
-  if (st != HATTN_OK) return st;
+  bool fused = false;
+  st = gemm(w->o_weight, H, Hq * 256, attn, (int)T, (long long)Hq * 256, y, H, ws + L.gemm, s, (const float*)x,
+            (float*)out, &fused);
+  if (st != HATTN_OK || fused) return st;
   return launch_residual_add((const float*)x, y, (float*)out, T * H, s) == hipSuccess ? HATTN_OK
                                                                                      : HATTN_ERR_LAUNCH;
 }

@@ -13,7 +13,8 @@
 // kSlots - 1 chunks stay in flight while one is computed, and the bf16 MFMA
 // 16x16x32 reads its fragments back from LDS. The four partial sums meet in
 // LDS (reusing the rings) and are added in a fixed order (wave 0 + 1 + 2 +
-// 3), then rounded once to bf16.
+// 3), then rounded once to bf16. With a residual (out_proj), the epilogue
+// also adds that bf16 value to the fp32 residual row and writes the fp32 sum.
 #include "hattn_device.h"
 #include "hattn_internal.h"
 
@@ -165,12 +166,27 @@ __global__ __launch_bounds__(256, 1) void skinny_gemm_kernel(SkinnyGemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       y[j] = ((red[0][t][c + j] + red[1][t][c + j]) + red[2][t][c + j]) + red[3][t][c + j];
-    uint4 o;
-    o.x = (uint32_t)float_to_bf16_bits(y[0]) | ((uint32_t)float_to_bf16_bits(y[1]) << 16);
-    o.y = (uint32_t)float_to_bf16_bits(y[2]) | ((uint32_t)float_to_bf16_bits(y[3]) << 16);
-    o.z = (uint32_t)float_to_bf16_bits(y[4]) | ((uint32_t)float_to_bf16_bits(y[5]) << 16);
-    o.w = (uint32_t)float_to_bf16_bits(y[6]) | ((uint32_t)float_to_bf16_bits(y[7]) << 16);
-    *(uint4*)(g.d + (size_t)t * g.ldd + n0 + c) = o;
+    uint16_t yb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) yb[j] = float_to_bf16_bits(y[j]);
+    if (g.out) {
+      // each element is read and written by this thread alone: out may be x
+      const size_t o = (size_t)t * g.ldd + n0 + c;
+      const float4 x0 = *(const float4*)(g.x + o), x1 = *(const float4*)(g.x + o + 4);
+      const float4 s0 = make_float4(x0.x + bf16_bits_to_float(yb[0]), x0.y + bf16_bits_to_float(yb[1]),
+                                    x0.z + bf16_bits_to_float(yb[2]), x0.w + bf16_bits_to_float(yb[3]));
+      const float4 s1 = make_float4(x1.x + bf16_bits_to_float(yb[4]), x1.y + bf16_bits_to_float(yb[5]),
+                                    x1.z + bf16_bits_to_float(yb[6]), x1.w + bf16_bits_to_float(yb[7]));
+      *(float4*)(g.out + o) = s0;
+      *(float4*)(g.out + o + 4) = s1;
+    } else {
+      uint4 o;
+      o.x = (uint32_t)yb[0] | ((uint32_t)yb[1] << 16);
+      o.y = (uint32_t)yb[2] | ((uint32_t)yb[3] << 16);
+      o.z = (uint32_t)yb[4] | ((uint32_t)yb[5] << 16);
+      o.w = (uint32_t)yb[6] | ((uint32_t)yb[7] << 16);
+      *(uint4*)(g.d + (size_t)t * g.ldd + n0 + c) = o;
+    }
   }
 }
 

@@ -138,9 +138,13 @@ struct RmsNormArgs {
 struct SkinnyGemmArgs {
   const uint16_t* w;  // [N][K]
   const uint16_t* a;  // [T] rows lda elements apart
-  uint16_t* d;        // [T] rows ldd elements apart
+  uint16_t* d;        // [T] rows ldd elements apart (unused when out is set)
   int N, K, T;
   long long lda, ldd;
+  // Optional residual epilogue: out = x + bf16(D) in fp32, [T] rows ldd
+  // elements apart (out may be x); d is not written then.
+  const float* x;
+  float* out;
 };
 
 // Kernel arguments travel by value; keep each struct within 4 KiB.

@@ -247,8 +247,10 @@ int hattn_decode_static(const hattn_layer_desc* desc, const void* q,
  *                                      in fp32 (out stays fp32)
  * Linear layers have no bias (page §5: attention_bias false). The GEMMs are
  * bf16 in and out with fp32 accumulation: for at most 64 tokens (decode
- * batches) this library's weight-streaming kernel, otherwise hipBLASLt
- * through one handle per device, created on first use. The first hipBLASLt
+ * batches) this library's weight-streaming kernel, whose out_proj
+ * epilogue also does the residual add (same rounding: the bf16 projection
+ * is added to the fp32 residual), otherwise hipBLASLt through one handle
+ * per device, created on first use. The first hipBLASLt
  * call of a GEMM shape outside stream capture times a few candidates on its
  * own buffers and waits for them (once per shape and process); later calls,
  * and calls under capture, do not wait.
