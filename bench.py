@@ -82,6 +82,23 @@ def counter_traffic(workload):
     return e.get("hbm_bytes_per_launch")
 
 
+def counter_clock():
+    """The prefill kernel's average shader clock and MFMA-busy fraction from
+    the committed rocprofv3 counter pass (GRBM_GUI_ACTIVE per XCD over the
+    dispatch time; SQ_VALU_MFMA_BUSY_CYCLES over the SIMD cycles), or None
+    when the summary is missing or the kernel's source has changed since."""
+    p = os.path.join(PROFILES, "prefill_mfma_counters.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    src = d.get("source")
+    if src not in KERNEL_SRC or d.get("source_sha256") != source_sha(KERNEL_SRC[src]):
+        return None
+    return {"sclk_GHz": d.get("avg_clock_GHz"), "mfma_busy": d.get("mfma_busy"), "dispatches": d.get("dispatches"),
+            "source": "profiles/prefill_mfma_counters.json"}
+
+
 def copy_calibration():
     """A plain device copy of known size (fp32 negation, 1 GiB read + 1 GiB
     written per launch), run under the same counters as the kernels to scale
@@ -161,40 +178,6 @@ def to_paged(torch, hb, ck, cv, page, seed):
     return hb.KVCache.paged(pool(ck), pool(cv), perm.view(B, n).to(torch.int32).to(ck.device))
 
 
-class ClockStamps:
-    """Counter rates over a region of the current stream: the library's stamp
-    kernel records, per block, the s_memtime and s_memrealtime counters before
-    and after the region, and events time it. Reports each counter's rate
-    (MHz of the region's event time); the shader clock is the s_memtime rate
-    where that counter follows the shader clock."""
-
-    def __init__(self, torch, hb, dev, blocks=8):
-        self.torch, self.hb = torch, hb
-        self.s0 = torch.zeros((blocks, 2), dtype=torch.int64, device=dev)
-        self.s1 = torch.zeros_like(self.s0)
-        self.e0 = torch.cuda.Event(enable_timing=True)
-        self.e1 = torch.cuda.Event(enable_timing=True)
-
-    def __enter__(self):
-        self.hb.debug_clock_stamp(self.s0, self.s0.shape[0])
-        self.e0.record()
-        return self
-
-    def __exit__(self, *exc):
-        self.e1.record()
-        self.hb.debug_clock_stamp(self.s1, self.s1.shape[0])
-
-    def rates(self):
-        self.torch.cuda.synchronize()
-        ms = self.e0.elapsed_time(self.e1)
-        a, b = self.s0.cpu(), self.s1.cpu()
-        n = a.shape[0]
-        mt = sum(int(b[i, 0]) - int(a[i, 0]) for i in range(n)) / n
-        rt = sum(int(b[i, 1]) - int(a[i, 1]) for i in range(n)) / n
-        return {"region_ms": round(ms, 4), "memtime_MHz": round(mt / (ms * 1e3), 1),
-                "memrealtime_MHz": round(rt / (ms * 1e3), 1)}
-
-
 def ceilings(torch, hb, dev, steps=5):
     """What the chip itself delivers, timed beside the path (event-timed,
     back to back): the library's plain streaming-read probe over 4 GiB and
@@ -226,15 +209,13 @@ def ceilings(torch, hb, dev, steps=5):
     fsink = torch.zeros(256 * 4, dtype=torch.float32, device=dev)
     iters = 8000
     hb.debug_mfma_probe(256, iters, fsink)
-    with ClockStamps(torch, hb, dev) as clk:
-        ms = time_calls(torch, lambda: hb.debug_mfma_probe(256, iters, fsink), steps, 1)
+    ms = time_calls(torch, lambda: hb.debug_mfma_probe(256, iters, fsink), steps, 1)
     fl = 256 * 4 * iters * 8 * 32768
     tf = fl / (ms * 1e-3) / 1e12
     # one 32x32x16 MFMA per 32 cycles per SIMD at full issue: the clock the
     # rate implies (1,024 SIMDs x 1,024 flop per cycle)
     res["mfma_bf16_32x32x16_probe"] = {"ms": round(ms, 4), "TFLOP_per_s": round(tf, 1),
-                                       "implied_sclk_GHz": round(tf * 1e12 / (1024 * 1024) / 1e9, 3),
-                                       "counters": clk.rates()}
+                                       "implied_sclk_GHz": round(tf * 1e12 / (1024 * 1024) / 1e9, 3)}
     a = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
     b = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
     ms = time_calls(torch, lambda: torch.mm(a, b), steps, 2)
@@ -456,8 +437,7 @@ def run(args):
     torch.cuda.synchronize()
     hb.hattn_profile_read(hb.PROFILE_PREFILL)
     hb.hattn_profile_enable(True)
-    with ClockStamps(torch, hb, dev) as clk:
-        ms = time_calls(torch, prefill, args.steps, 0)
+    ms = time_calls(torch, prefill, args.steps, 0)
     hb.hattn_profile_enable(False)
     n, attn_total = hb.hattn_profile_read(hb.PROFILE_PREFILL)
     attn_ms = attn_total / max(n, 1)
@@ -470,7 +450,7 @@ def run(args):
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
         "traffic": counter_traffic("prefill_full_s8192"),
         "kernel": "prefill_attn_kernel", "flop_per_launch": flops, "avg_launch_ms": round(attn_ms, 5),
-        "launches_timed": n, "counters_during_timed_steps": clk.rates(),
+        "launches_timed": n, "clock_from_counters": counter_clock(),
     }
     del inp, cache, out, ws
     torch.cuda.empty_cache()

@@ -109,7 +109,6 @@ _SIGS = {
                                      ctypes.POINTER(ctypes.c_uint64)]),
     "hattn_kv_cache_at": (ctypes.c_int, [ctypes.POINTER(KvLayerPlan), _P, ctypes.POINTER(KvCacheC)]),
     "hattn_debug_index_probe": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _I, _I, _I, _I, _P, _P, _P, _P]),
-    "hattn_debug_clock_stamp": (ctypes.c_int, [_P, _I, _P]),
     "hattn_debug_read_probe": (ctypes.c_int, [_P, ctypes.c_size_t, _I, _P, _P]),
     "hattn_debug_mfma_probe": (ctypes.c_int, [_I, _I, _P, _P]),
     "hattn_profile_enable": (ctypes.c_int, [ctypes.c_int]),
@@ -488,13 +487,6 @@ def hattn_profile_read(kind):
     ms = ctypes.c_double()
     _check("hattn_profile_read", lib().hattn_profile_read(kind, ctypes.byref(n), ctypes.byref(ms)))
     return int(n.value), float(ms.value)
-
-
-def debug_clock_stamp(out, blocks=8):
-    """Writes (shader clock counter, 100 MHz reference counter) per block into
-    the int64 device tensor out [blocks, 2] on the current stream."""
-    _need(out, "out", torch.int64, (blocks, 2))
-    _check("hattn_debug_clock_stamp", lib().hattn_debug_clock_stamp(_ptr(out), blocks, _stream(out.device)))
 
 
 def debug_read_probe(buf, blocks, sink):

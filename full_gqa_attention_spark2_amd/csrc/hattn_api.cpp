@@ -634,13 +634,6 @@ int hattn_profile_read(int kind, int64_t* count, double* total_ms) {
   return st;
 }
 
-int hattn_debug_clock_stamp(uint64_t* out, int32_t blocks, hipStream_t stream) {
-  if (blocks < 1 || blocks > 1024) return HATTN_ERR_SHAPE;
-  if (!out) return HATTN_ERR_NULL;
-  if ((uintptr_t)out & 7u) return HATTN_ERR_ALIGN;
-  return from_hip(launch_clock_stamp((unsigned long long*)out, blocks, stream));
-}
-
 int hattn_debug_read_probe(const void* buf, size_t bytes, int32_t blocks, uint32_t* sink, hipStream_t stream) {
   if (blocks < 1 || bytes % 16) return HATTN_ERR_SHAPE;
   if (bytes == 0) return HATTN_OK;

@@ -200,7 +200,6 @@ hipError_t launch_rms_norm(const RmsNormArgs& a, hipStream_t s);
 bool skinny_gemm_fits(int N, int K, int T, long long lda, long long ldd, const void* w, const void* a,
                       const void* d);
 hipError_t launch_skinny_gemm(const SkinnyGemmArgs& g, hipStream_t s);
-hipError_t launch_clock_stamp(unsigned long long* out, int blocks, hipStream_t s);
 hipError_t launch_read_probe(const void* buf, size_t bytes, int blocks, uint32_t* sink, hipStream_t s);
 hipError_t launch_mfma_probe(int blocks, int iters, float* sink, hipStream_t s);
 hipError_t launch_residual_add(const float* x, const uint16_t* y, float* out, long long n, hipStream_t s);

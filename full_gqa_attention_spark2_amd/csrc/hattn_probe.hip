@@ -1,8 +1,5 @@
 // Measurement probes: what the chip itself delivers, measured beside the
 // attention kernels so that their roofline fractions can be read against it.
-//   - clock_stamp_kernel: the shader clock counter and the constant 100 MHz
-//     reference counter, one pair per block, so that two stamps around a
-//     timed region give the average shader clock over it;
 //   - read_probe_kernel: a plain streaming read (16 B per lane, eight loads in
 //     flight per thread), the practical HBM read rate at a given size;
 //   - mfma_probe_kernel: back-to-back bf16 MFMA 32x32x16 on pseudo-random
@@ -15,15 +12,6 @@
 namespace hattn {
 
 namespace {
-
-__global__ void clock_stamp_kernel(unsigned long long* out) {
-  if (threadIdx.x == 0) {
-    const unsigned long long t = __builtin_amdgcn_s_memtime();
-    const unsigned long long r = __builtin_amdgcn_s_memrealtime();
-    out[2 * blockIdx.x] = t;
-    out[2 * blockIdx.x + 1] = r;
-  }
-}
 
 // Block b streams its contiguous share of the buffer; every thread keeps
 // eight 16-byte loads in flight and folds them into one word.
@@ -76,11 +64,6 @@ __global__ __launch_bounds__(256, 1) void mfma_probe_kernel(int iters, float* si
 }
 
 }  // namespace
-
-hipError_t launch_clock_stamp(unsigned long long* out, int blocks, hipStream_t s) {
-  hipLaunchKernelGGL(clock_stamp_kernel, dim3(blocks), dim3(64), 0, s, out);
-  return hipGetLastError();
-}
 
 hipError_t launch_read_probe(const void* buf, size_t bytes, int blocks, uint32_t* sink, hipStream_t s) {
   hipLaunchKernelGGL(read_probe_kernel, dim3(blocks), dim3(256), 0, s, (const u32x4*)buf, bytes / 16, sink);

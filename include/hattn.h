@@ -375,10 +375,6 @@ int hattn_debug_index_probe(const hattn_layer_desc* desc, int32_t kv_kind,
 
 /* Measurement probes (not on the attention path; used by the benchmark to
  * put the kernels' rates beside what the chip itself delivers).
- * hattn_debug_clock_stamp: `blocks` one-wave blocks each write the shader
- *   clock counter and the constant 100 MHz reference counter (s_memtime,
- *   s_memrealtime) to out[2b], out[2b+1] (device uint64 [blocks][2]); two
- *   stamps around a timed region give the average shader clock over it.
  * hattn_debug_read_probe: streams `bytes` (a multiple of 16) of device
  *   memory with `blocks` 256-thread blocks, 16-byte loads, eight in flight
  *   per thread; sink: device uint32 [blocks], written only in a case random
@@ -387,7 +383,6 @@ int hattn_debug_index_probe(const hattn_layer_desc* desc, int32_t kv_kind,
  *   rounds of 8 independent bf16 MFMA 32x32x16 (262,144 flop per wave and
  *   round) on pseudo-random operands; sink: device float [blocks][4].
  * Errors: HATTN_ERR_SHAPE, _NULL, _ALIGN as for the other entry points. */
-int hattn_debug_clock_stamp(uint64_t* out, int32_t blocks, hipStream_t stream);
 int hattn_debug_read_probe(const void* buf, size_t bytes, int32_t blocks,
                            uint32_t* sink, hipStream_t stream);
 int hattn_debug_mfma_probe(int32_t blocks, int32_t iters, float* sink,
