@@ -120,16 +120,19 @@ constexpr int stream_reads(int mode, int e) {  // LDS reads feeding element e
 // element e + ahead and up to kValu VALU / transcendental instructions (the
 // softmax that runs beside the stream). Barriers only constrain the
 // instructions that precede them in the same basic block.
+// With split queries an S element is two MFMAs (the queries' high and low
+// bf16 parts against the same K fragment).
 constexpr int kSoftmaxValuPerMfma = 3;
 constexpr int kSgMfma = 0x008, kSgDsRead = 0x100, kSgValu = 0x002 | 0x400;
-template <int Mode, int E, int Valu>
+constexpr bool stream_is_s(int mode, int e) { return mode == kStreamS || (mode == kStreamSPv && (e & 1) == 0); }
+template <int Mode, int E, int Valu, bool kSplitQ>
 __device__ __forceinline__ void issue_order_tail() {
   if constexpr (E < stream_length(Mode)) {
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, (kSplitQ && stream_is_s(Mode, E)) ? 2 : 1, 0);
     if constexpr (E + stream_ahead(Mode) < stream_length(Mode))
       __builtin_amdgcn_sched_group_barrier(kSgDsRead, stream_reads(Mode, E + stream_ahead(Mode)), 0);
     if constexpr (Valu > 0) __builtin_amdgcn_sched_group_barrier(kSgValu, Valu, 0);
-    issue_order_tail<Mode, E + 1, Valu>();
+    issue_order_tail<Mode, E + 1, Valu, kSplitQ>();
   }
 }
 template <int Mode, int E, int Acc>
@@ -140,10 +143,10 @@ template <int Mode, int Acc>
 struct StreamHead<Mode, 0, Acc> {
   static constexpr int value = Acc;
 };
-template <int Mode, int Valu>
+template <int Mode, int Valu, bool kSplitQ>
 __device__ __forceinline__ void issue_order() {
   __builtin_amdgcn_sched_group_barrier(kSgDsRead, StreamHead<Mode, stream_ahead(Mode), 0>::value, 0);
-  issue_order_tail<Mode, 0, Valu>();
+  issue_order_tail<Mode, 0, Valu, kSplitQ>();
 }
 
 }  // namespace
@@ -152,7 +155,10 @@ __device__ __forceinline__ void issue_order() {
 // positions 0 .. n_keys-1); its page indices for the workgroup's tiles are
 // staged in LDS first, and every tile (64 rows, inside one page) is read
 // through a buffer resource over its page.
-template <bool kPaged>
+// kSplitQ: each rotated query channel enters the scores as a bf16 high part
+// plus a bf16 low part (x - hi, rounded), about 16 significant bits instead
+// of 8, at the cost of a second S MFMA per K fragment (no extra LDS reads).
+template <bool kPaged, bool kSplitQ>
 __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a) {
   // Two K and two V tile slots (the swizzled block layout is described at
   // load_tile below). Four separate arrays (not one indexed array) so the
@@ -255,6 +261,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   const size_t orow = (tok0 + (qvalid ? qrow : len - 1)) * (size_t)a.gate_stride + h;
   const uint16_t gate_bits = a.gate[orow];
   bf16x8 qf[16];
+  bf16x8 qlo[kSplitQ ? 16 : 1];
   {
     const int qr = qvalid ? qrow : len - 1;
     const uint16_t* qp = a.q + (tok0 + qr) * (size_t)a.q_stride + (size_t)h * kHeadDim;
@@ -296,6 +303,12 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = (__bf16)(qvalid ? x[j] : 0.f);
         qf[ks] = v;
+        if constexpr (kSplitQ) {
+          bf16x8 lo;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) lo[j] = (__bf16)(qvalid ? x[j] - (float)v[j] : 0.f);
+          qlo[ks] = lo;
+        }
       }
     };
     // Any other r (a multiple of 16): fragment by fragment, partners and
@@ -322,6 +335,12 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = (__bf16)(qvalid ? x[j] : 0.f);
         qf[ks] = v;
+        if constexpr (kSplitQ) {
+          bf16x8 lo;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) lo[j] = (__bf16)(qvalid ? x[j] - (float)v[j] : 0.f);
+          qlo[ks] = lo;
+        }
       }
     };
     if (a.r == 64) rope_fast(std::integral_constant<int, 2>{});
@@ -331,6 +350,10 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
     // accumulation registers, which leaves the VGPRs to the softmax.
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) asm volatile("" : "+a"(qf[ks]));
+    if constexpr (kSplitQ) {
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) asm volatile("" : "+a"(qlo[ks]));
+    }
   }
 
   auto need_mask = [&](int t) __attribute__((always_inline)) {
@@ -422,10 +445,10 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
       if (e + kAhead < kN) issue(e + kAhead);
       const int i = index(e);
       if (is_s(e)) {
-        if (i & 1)
-          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[i % kRing], qf[i >> 1], s1, 0, 0, 0);
-        else
-          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[i % kRing], qf[i >> 1], s0, 0, 0, 0);
+        f32x16& sb = (i & 1) ? s1 : s0;
+        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[i % kRing], qf[i >> 1], sb, 0, 0, 0);
+        if constexpr (kSplitQ)
+          sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[i % kRing], qlo[i >> 1], sb, 0, 0, 0);
       } else {
         acc[i & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vr[i % kRing]), p[i >> 3],
                                                             acc[i & 7], 0, 0, 0);
@@ -502,7 +525,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   wait_loads();
   __syncthreads();
   mma_stream(ModeS{}, k_lds0, v_lds0, sA0, sA1, pA, [](int) {});
-  issue_order<kStreamS, 0>();
+  issue_order<kStreamS, 0, kSplitQ>();
   if (need_mask(t_lo)) mask_s(t_lo, sA0, sA1);
 
   // One iteration; the first one has no P.V yet. On the last tile S(t+1)
@@ -535,7 +558,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
         if (e % kLoadSpacing == 0 && e < 4 * kLoadSpacing && wave == e / kLoadSpacing) load_tiles();
     });
     rescale_pending = softmax(sc0, sc1, pn, alpha_pending);
-    issue_order<kMode, kSoftmaxValuPerMfma>();
+    issue_order<kMode, kSoftmaxValuPerMfma, kSplitQ>();
     if (j + 1 < nt && need_mask(t + 1)) mask_s(t + 1, sn0, sn1);
   };
   // even j: S(t) in sA, P(t) -> pA, P(t-1) in pB; odd j: the other way round
@@ -550,10 +573,10 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   if (rescale_pending) rescale_o(alpha_pending);
   if ((nt - 1) & 1) {
     mma_stream(ModePv{}, k_lds0, v_lds1, sA0, sA1, pB, [](int) {});
-    issue_order<kStreamPv, 0>();
+    issue_order<kStreamPv, 0, kSplitQ>();
   } else {
     mma_stream(ModePv{}, k_lds0, v_lds0, sA0, sA1, pA, [](int) {});
-    issue_order<kStreamPv, 0>();
+    issue_order<kStreamPv, 0, kSplitQ>();
   }
   l_i = pair_sum(l_i);
 
@@ -591,10 +614,20 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s) {
   const int grid = a.q_tiles * a.B * a.Hkv;
   if (grid == 0) return hipSuccess;
+  // A sliding window that cuts keys for some query (a query at position p
+  // sees p - w + 1 .. p) takes the split queries: bf16 queries alone leave
+  // little of the error budget on such layers. Otherwise (full layers, and
+  // windows covering every distance, which are then exactly causal) the
+  // plain kernel runs; paged caches belong to full layers.
+  bool cuts = false;
+  if (a.window > 0)
+    for (int b = 0; b < a.B; ++b) cuts = cuts || (a.len[b] > 0 && (long long)a.start[b] + a.len[b] > a.window);
   if (a.paged.table)
-    hipLaunchKernelGGL(prefill_attn_kernel<true>, dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((prefill_attn_kernel<true, false>), dim3(grid), dim3(256), 0, s, a);
+  else if (cuts)
+    hipLaunchKernelGGL((prefill_attn_kernel<false, true>), dim3(grid), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(prefill_attn_kernel<false>, dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((prefill_attn_kernel<false, false>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -405,14 +405,19 @@ def test_prefill_window_one_and_peaky():
     desc, inp, ck, cv, cache, out = run_prefill("sliding", 1, 300, 16, 4, [0], 4, "linear", 300, window=1)
     ref, _ = oracle_prefill(desc, inp, ck, cv, [0], "linear", 300)
     check("prefill window=1", out.cpu(), ref)
-    # Peaky softmax: queries 8x larger make scores 8x larger. The kernel feeds
-    # the rotated queries to the MFMA as bf16 (relative error 2^-9 per
-    # channel), so the score error grows 8x with them; this stress case is
-    # held to the standard bars scaled by that factor (8e-2 max-abs, 2.4e-2
-    # relative RMS), not to the bars of the N(0,1) workloads.
-    desc, inp, ck, cv, cache, out = run_prefill("sliding", 1, 512, 16, 4, [0], 5, "ring", 512, q_scale=8.0)
+    # Peaky softmax: queries 8x larger make scores 8x larger, and the score
+    # error grows with the query rounding. Sliding layers whose window cuts
+    # keys (here every row past 511) feed the queries as bf16 high + low
+    # parts (~16 significant bits); bf16 queries alone could not meet the
+    # bars (the CPU error model's test shows that for any pipeline rounding
+    # the queries to bf16). The relative RMS bar is the standard one. The
+    # max-abs bar is doubled: where one key dominates a row, its probability
+    # is 2^(s - m) against the lazily moved running max m (m moves only by
+    # more than 2^8), so it is not exactly 1 and its bf16 rounding (2^-9
+    # relative) reaches outputs of size 2-4.
+    desc, inp, ck, cv, cache, out = run_prefill("sliding", 1, 768, 16, 4, [0], 5, "ring", 512, q_scale=8.0)
     ref, _ = oracle_prefill(desc, inp, ck, cv, [0], "ring", 512)
-    check("prefill peaky softmax (q x8)", out.cpu(), ref, max_abs=8 * MAX_ABS, rel_rms=8 * REL_RMS)
+    check("prefill peaky softmax (q x8)", out.cpu(), ref, max_abs=2 * MAX_ABS)
 
 
 def test_chunked_prefill_equals_monolithic():
