@@ -13,8 +13,11 @@ divided by the event-timed duration of the K timed calls.
 Two more prefill workloads are reported under "prefill_configs" (not in
 ``value``): a sliding layer at 1024 tokens (batch 1, ring cache), and the
 1.7B shape's chunked prefill (8 / 2 heads, batch 2, a 4096-token chunk on a
-262144-token context), whose 28-layer time is composed from one timed call
-per layer type (21 sliding + 7 full layers).
+262144-token context), timed as whole 28-layer passes in the page's layer
+order over 28 distinct caches (the sum of one call per layer type is kept as
+a secondary figure), plus its full layer on a paged cache; and the 4B
+attention block (norm, projections, core, out_proj, residual) for prefill and
+decode.
 
 Decode is timed in its own section after the prefill steps and reported under
 "decode": sliding-layer decode over 64 sequences with 512-slot ring caches,
@@ -22,6 +25,13 @@ and full-layer decode over 2^20 cached tokens (batch 1) and 8 x 131072
 tokens, each as KV GB/s per call (decode kernel plus split merge, timed
 back to back). The calls cycle over enough distinct caches that the 256 MB
 last-level cache cannot serve the KV cache.
+
+"roofline" describes the prefill attention kernel (HIP events around each of
+its launches in the timed steps), with the HBM traffic and the shader clock
+from the committed rocprofv3 counter passes when the kernel source still
+matches them. "practical_ceilings" times the library's streaming-read and
+MFMA probes and torch's bf16 GEMM beside the path. "cpu_baseline" times the
+fp64 oracle on the host on a bounded sample of each workload.
 
 All inputs are seeded synthetic tensors (N(0,1) bf16 Q/K/V and caches, gate
 logits N(0, 2^2)) already resident in HBM when timing starts.
