@@ -559,6 +559,12 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
     });
     rescale_pending = softmax(sc0, sc1, pn, alpha_pending);
     issue_order<kMode, kSoftmaxValuPerMfma, kSplitQ>();
+    // The softmax's results are used here, ahead of the mask branch: nothing
+    // below needs them before the next step, and without this use the
+    // compiler may sink the whole softmax past that branch, out of the
+    // matrix-core stream it is interleaved with.
+    asm volatile("" : "+v"(pn[0]), "+v"(pn[1]), "+v"(pn[2]), "+v"(pn[3]), "+v"(alpha_pending), "+v"(l_i),
+                 "+v"(m_i));
     if (j + 1 < nt && need_mask(t + 1)) mask_s(t + 1, sn0, sn1);
   };
   // even j: S(t) in sA, P(t) -> pA, P(t-1) in pB; odd j: the other way round
