@@ -222,13 +222,24 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   // reads below free of bank conflicts. Each wave loads blocks 8w .. 8w+7.
   // Rows past the valid keys re-read the last valid key; their scores are
   // masked, so they contribute exactly zero.
-  const uint32_t k_chunk0 = 16u * ((lane & 7) ^ (lane >> 3));
-  const uint32_t k_chunk1 = 16u * ((lane & 7) ^ (lane >> 3) ^ 1);
-  const uint32_t v_chunk = 16u * ((lane & 7) ^ ((2 * (lane >> 3)) & 7));
-  auto load_tile = [&](__amdgpu_buffer_rsrc_t rs, uint32_t chunk0, uint32_t chunk1, int t, char* slot)
-      __attribute__((always_inline)) {
+  // With split queries the registers run short: the lane's row and chunk
+  // are then recomputed from the lane id at each tile load (asm, so the
+  // compiler neither hoists nor keeps them). Held across the tile loop they
+  // are among the first values the register allocator spills, and a reload
+  // from scratch inside the matrix-core stream stalls the wave on its memory
+  // counter. The plain kernel has registers to spare and keeps them.
+  auto load_lane = [&]() __attribute__((always_inline)) {
+    uint32_t l = (uint32_t)lane;
+    if constexpr (kSplitQ) asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+  };
+  auto load_tile = [&](__amdgpu_buffer_rsrc_t rs, bool is_v, int t, char* slot) __attribute__((always_inline)) {
+    const uint32_t ln = load_lane();
+    const uint32_t r = ln >> 3, c = ln & 7;
+    const uint32_t chunk0 = 16u * (is_v ? (c ^ ((2 * r) & 7)) : (c ^ r));
+    const uint32_t chunk1 = 16u * (is_v ? (c ^ ((2 * r) & 7)) : (c ^ r ^ 1));
     char* dst = slot + wave * 8 * 1024;
-    const int row0 = t * kBN + 16 * wave + (lane >> 3);
+    const int row0 = t * kBN + 16 * wave + (int)r;
     const int base_row = kPaged ? t * kBN / ps * ps : 0;  // first row of the tile's page
     const uint32_t off0 = (uint32_t)(min(row0, nk - 1) - base_row) * 512u + chunk0;
     const uint32_t off1 = (uint32_t)(min(row0 + 8, nk - 1) - base_row) * 512u + chunk1;
@@ -241,7 +252,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
     return slab_rsrc(pool + ((size_t)pg * a.Hkv + kvh) * (size_t)ps * kHeadDim, (uint32_t)ps * 512u);
   };
   auto load_k = [&](int t, char* slot) __attribute__((always_inline)) {
-    load_tile(kPaged ? page_rsrc(a.kc, t) : krs, k_chunk0, k_chunk1, t, slot);
+    load_tile(kPaged ? page_rsrc(a.kc, t) : krs, false, t, slot);
   };
 
   // The first K tiles: requested right after the query loads below, so they
@@ -546,8 +557,8 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
     const __amdgpu_buffer_rsrc_t rk = kPaged ? page_rsrc(a.kc, tk) : krs;
     const __amdgpu_buffer_rsrc_t rv = kPaged ? page_rsrc(a.vc, t) : vrs;
     auto load_tiles = [&]() __attribute__((always_inline)) {
-      if (j + 2 < nt) load_tile(rk, k_chunk0, k_chunk1, t + 2, kf);
-      load_tile(rv, v_chunk, v_chunk, t, vf);
+      if (j + 2 < nt) load_tile(rk, false, t + 2, kf);
+      load_tile(rv, true, t, vf);
     };
     // O holds P.V up to tile t-2 plus (below) tile t-1, all relative to the
     // max before softmax(t-1); a max move found by softmax(t-1) is applied
