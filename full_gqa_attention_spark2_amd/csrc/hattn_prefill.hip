@@ -631,17 +631,14 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s) {
   const int grid = a.q_tiles * a.B * a.Hkv;
   if (grid == 0) return hipSuccess;
-  // A sliding window that cuts keys for some query (a query at position p
-  // sees p - w + 1 .. p) takes the split queries: bf16 queries alone leave
-  // little of the error budget on such layers. Otherwise (full layers, and
-  // windows covering every distance, which are then exactly causal) the
-  // plain kernel runs; paged caches belong to full layers.
-  bool cuts = false;
-  if (a.window > 0)
-    for (int b = 0; b < a.B; ++b) cuts = cuts || (a.len[b] > 0 && (long long)a.start[b] + a.len[b] > a.window);
+  // Sliding-window layers take the split queries: bf16 queries alone leave
+  // little of the error budget there. The choice is per layer type, not per
+  // call, so a layer's results do not depend on how its prefill is chunked.
+  // Full layers (and paged caches, which belong to them) run the plain
+  // kernel.
   if (a.paged.table)
     hipLaunchKernelGGL((prefill_attn_kernel<true, false>), dim3(grid), dim3(256), 0, s, a);
-  else if (cuts)
+  else if (a.window > 0)
     hipLaunchKernelGGL((prefill_attn_kernel<false, true>), dim3(grid), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((prefill_attn_kernel<false, false>), dim3(grid), dim3(256), 0, s, a);

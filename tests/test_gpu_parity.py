@@ -168,17 +168,23 @@ def test_gpu_gate_and_window_invariants():
         outs.append(hb.hattn_prefill(desc, d["q"], d["k"], d["v"], d["gate"], [0], cache))
     torch.cuda.synchronize()
     assert torch.equal(outs[0], (outs[1].float() * 0.5).to(torch.bfloat16))
-    # a window covering every query-key distance gives exactly the causal result
+    # a window covering every query-key distance cuts nothing: bitwise the
+    # result of a far wider window (sliding layers all run the split-query
+    # kernel), and the oracle's causal attention at the standard bars
     S = 300
-    inp = to_dev(synth.prefill_inputs(1, S, 16, 4, seed=141))
+    inp_h = synth.prefill_inputs(1, S, 16, 4, seed=141)
+    inp = to_dev(inp_h)
     full = hb.layer_desc("full")
-    wide = hb.layer_desc("sliding", rope_theta=full.rope_theta, rotary_fraction=full.rotary_fraction, window=S + 7)
-    c1 = hb.KVCache.empty(1, 4, S, "linear")
-    c2 = hb.KVCache.empty(1, 4, S, "linear")
-    o1 = hb.hattn_prefill(full, inp["q"], inp["k"], inp["v"], inp["gate"], [0], c1)
-    o2 = hb.hattn_prefill(wide, inp["q"], inp["k"], inp["v"], inp["gate"], [0], c2)
+    outs = []
+    for w in (S + 7, 1 << 20):
+        wide = hb.layer_desc("sliding", rope_theta=full.rope_theta, rotary_fraction=full.rotary_fraction, window=w)
+        c = hb.KVCache.empty(1, 4, S, "linear")
+        outs.append(hb.hattn_prefill(wide, inp["q"], inp["k"], inp["v"], inp["gate"], [0], c))
     torch.cuda.synchronize()
-    assert torch.equal(o1, o2)
+    assert torch.equal(outs[0], outs[1])
+    z = torch.zeros(1, 4, S, 256, dtype=torch.bfloat16)
+    ref, _ = oracle_prefill(full, inp_h, z, z, [0], "linear", S)
+    check("prefill window covering every distance vs causal", outs[0].cpu(), ref)
 
 
 def test_decode_split_count_does_not_change_the_result():
@@ -406,9 +412,9 @@ def test_prefill_window_one_and_peaky():
     ref, _ = oracle_prefill(desc, inp, ck, cv, [0], "linear", 300)
     check("prefill window=1", out.cpu(), ref)
     # Peaky softmax: queries 8x larger make scores 8x larger, and the score
-    # error grows with the query rounding. Sliding layers whose window cuts
-    # keys (here every row past 511) feed the queries as bf16 high + low
-    # parts (~16 significant bits); bf16 queries alone could not meet the
+    # error grows with the query rounding. Sliding layers feed the queries as
+    # bf16 high + low parts (~16 significant bits); rows past 511 also see the
+    # window cut keys. bf16 queries alone could not meet the
     # bars (the CPU error model's test shows that for any pipeline rounding
     # the queries to bf16). The relative RMS bar is the standard one. The
     # max-abs bar is doubled: where one key dominates a row, its probability
