@@ -742,6 +742,13 @@ def test_block_decode_token_counts(B):
     ref, _, _ = O.block_decode_ref(x, w["norm"], w["qkvg"], w["o"], 1e-6, pos, ck, cv, Hq=16, Hkv=4, kind="ring",
                                    window=512, theta=desc.rope_theta, rotary_fraction=desc.rotary_fraction)
     check_block(f"block decode B={B}", out.cpu(), ref, x)
+    # in place (out is x): the out_proj epilogue reads each residual element
+    # before it writes it, so the bits are the same
+    cache2 = hb.KVCache(ck.to(DEV), cv.to(DEV), "ring")
+    xi = x.to(DEV)
+    hb.hattn_block_decode(desc, wd, xi, torch.as_tensor(pos).to(DEV), int(pos.max()), cache2, out=xi)
+    torch.cuda.synchronize()
+    assert torch.equal(xi, out)
 
 
 def cache_after_varlen_prefill(ck, cv, k_hat, v, cu, start, kind, cap):
