@@ -293,33 +293,43 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
 #pragma unroll
         for (int u = 0; u < 4; ++u) cs[pp][u] = *(const uint4*)(tp + pp * 16 + (lane >> 5) * 8 + 2 * u);
       load_first_tiles();
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) {
-        float x[8];
-        unpack8(raw[ks], x);
-        if (ks < 2 * NP) {
-          const bool first = ks < NP;
-          const int pp = first ? ks : ks - NP;
-          float xp[8];
-          unpack8(raw[first ? ks + NP : ks - NP], xp);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const uint4 w = cs[pp][j >> 1];
-            const float2 t = (j & 1) ? make_float2(__uint_as_float(w.z), __uint_as_float(w.w))
-                                     : make_float2(__uint_as_float(w.x), __uint_as_float(w.y));
-            x[j] = first ? x[j] * t.x - xp[j] * t.y : x[j] * t.x + xp[j] * t.y;
-          }
-        }
+      // Rows past the sequence's end hold the last row's queries (qr is
+      // clamped): their columns repeat a column of the same wave, so they
+      // change none of its decisions, and their outputs are not stored.
+      auto put = [&](int ks, const float* x) __attribute__((always_inline)) {
         bf16x8 v;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = (__bf16)(qvalid ? x[j] : 0.f);
+        for (int j = 0; j < 8; ++j) v[j] = (__bf16)x[j];
         qf[ks] = v;
         if constexpr (kSplitQ) {
           bf16x8 lo;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) lo[j] = (__bf16)(qvalid ? x[j] - (float)v[j] : 0.f);
+          for (int j = 0; j < 8; ++j) lo[j] = (__bf16)(x[j] - (float)v[j]);
           qlo[ks] = lo;
         }
+      };
+      // each rotated pair (pp, pp + NP) is unpacked once
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) {
+        float xa[8], xb[8], ra[8], rb[8];
+        unpack8(raw[pp], xa);
+        unpack8(raw[pp + NP], xb);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint4 w = cs[pp][j >> 1];
+          const float2 t = (j & 1) ? make_float2(__uint_as_float(w.z), __uint_as_float(w.w))
+                                   : make_float2(__uint_as_float(w.x), __uint_as_float(w.y));
+          ra[j] = xa[j] * t.x - xb[j] * t.y;
+          rb[j] = xb[j] * t.x + xa[j] * t.y;
+        }
+        put(pp, ra);
+        put(pp + NP, rb);
+      }
+      // channels past r pass through: their bf16 bits are the fragments
+#pragma unroll
+      for (int ks = 2 * NP; ks < 16; ++ks) {
+        qf[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
+        if constexpr (kSplitQ) qlo[ks] = bf16x8{};
       }
     };
     // Any other r (a multiple of 16): fragment by fragment, partners and
