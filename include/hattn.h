@@ -157,7 +157,12 @@ size_t hattn_prefill_workspace_size(const hattn_layer_desc* desc,
  * 128; the key rows of one (sequence, KV head) -- a linear cache's
  * capacity, or window - 1 + S for a ring; paged caches are addressed page
  * by page and exempt -- at most 2^23; ceil(S / 32) * B * num_kv_heads
- * below 2^31. */
+ * below 2^31.
+ * Numerics: keys are rotated in fp64 and cached as bf16 (one rounding);
+ * the scores take the rotated queries as bf16 on full layers and as a bf16
+ * high part plus a bf16 low part (~16 significant bits) on sliding layers;
+ * products accumulate in fp32, probabilities enter P.V as bf16, and the
+ * gated output is rounded once to bf16. */
 int hattn_prefill(const hattn_layer_desc* desc, const void* q, const void* k,
                   const void* v, const void* gate, int32_t batch,
                   int32_t seq_len, const int32_t* start_pos,
