@@ -726,10 +726,12 @@ def test_block_prefill_and_decode(layer, hidden, Hq, Hkv, kind, cap):
     check_block(f"block decode {layer} hidden={hidden}", od.cpu(), ref_d, xd)
 
 
-@pytest.mark.parametrize("B", [17, 64])
+@pytest.mark.parametrize("B", [1, 17, 64, 65])
 def test_block_decode_token_counts(B):
-    # decode batches of 17 and 64 sequences: the weight-streaming GEMM's
-    # partial and full token blocks
+    # decode batches of 1, 17 and 64 sequences: the weight-streaming GEMM's
+    # partial and full token blocks (its out_proj epilogue adds the
+    # residual); 65 sequences: past its limit, hipBLASLt and the separate
+    # residual add
     desc = hb.layer_desc("sliding")
     w, wd = _block(2560, 16, 4, seed=150)
     ck = synth.cache_tensor(B, 4, 512, seed=151)
