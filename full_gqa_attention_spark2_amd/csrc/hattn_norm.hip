@@ -42,7 +42,11 @@ __device__ __forceinline__ uint4 pack8f(const float* x) {
 
 // One block per token: y = bf16(w * x / sqrt(mean(x^2) + eps)) from the
 // fp32 residual stream x, computed in fp32 (page §5: the norm is computed in
-// fp32, multiplied by the weight, and cast back to the model dtype).
+// fp32, multiplied by the weight, and cast back to the model dtype). Rows of
+// up to kNormHeld chunks per thread (hidden <= 8192) stay in registers, and
+// their weights are loaded with them: one round trip to memory instead of
+// two. Each thread sums its chunks in the same order either way.
+constexpr int kNormHeld = 4;
 __global__ __launch_bounds__(kNormThreads) void rms_norm_kernel(RmsNormArgs a) {
   __shared__ float part[kNormThreads / 64];
   const int t = threadIdx.x;
@@ -50,12 +54,32 @@ __global__ __launch_bounds__(kNormThreads) void rms_norm_kernel(RmsNormArgs a) {
   uint4* y = (uint4*)(a.y + (size_t)blockIdx.x * a.H);
   const uint4* w = (const uint4*)a.w;
   const int n = a.H / 8;
+  const bool held = n <= kNormHeld * kNormThreads;
+  float v[kNormHeld][8];
+  uint4 wv[kNormHeld];
   float ss = 0.f;
-  for (int c = t; c < n; c += kNormThreads) {
-    float v[8];
-    load8f32(x + 8 * c, v);
+  if (held) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) ss = fmaf(v[j], v[j], ss);
+    for (int i = 0; i < kNormHeld; ++i) {
+      const int c = t + i * kNormThreads;
+      if (c < n) {
+        load8f32(x + 8 * c, v[i]);
+        wv[i] = w[c];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kNormHeld; ++i)
+      if (t + i * kNormThreads < n) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss = fmaf(v[i][j], v[i][j], ss);
+      }
+  } else {
+    for (int c = t; c < n; c += kNormThreads) {
+      float u[8];
+      load8f32(x + 8 * c, u);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss = fmaf(u[j], u[j], ss);
+    }
   }
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
   if ((t & 63) == 0) part[t >> 6] = ss;
@@ -64,13 +88,27 @@ __global__ __launch_bounds__(kNormThreads) void rms_norm_kernel(RmsNormArgs a) {
 #pragma unroll
   for (int i = 0; i < kNormThreads / 64; ++i) tot += part[i];
   const float r = rsqrtf(tot / (float)a.H + a.eps);
-  for (int c = t; c < n; c += kNormThreads) {
-    float v[8], g[8];
-    load8f32(x + 8 * c, v);
-    unpack8f(w[c], g);
+  if (held) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = v[j] * r * g[j];
-    y[c] = pack8f(v);
+    for (int i = 0; i < kNormHeld; ++i) {
+      const int c = t + i * kNormThreads;
+      if (c < n) {
+        float g[8];
+        unpack8f(wv[i], g);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[i][j] = v[i][j] * r * g[j];
+        y[c] = pack8f(v[i]);
+      }
+    }
+  } else {
+    for (int c = t; c < n; c += kNormThreads) {
+      float u[8], g[8];
+      load8f32(x + 8 * c, u);
+      unpack8f(w[c], g);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) u[j] = u[j] * r * g[j];
+      y[c] = pack8f(u);
+    }
   }
 }
 
