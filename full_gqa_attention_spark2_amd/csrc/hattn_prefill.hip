@@ -25,7 +25,9 @@
 // stream (wave w before element kLoadSpacing * w): the CU's load pipe takes
 // the four shares one after another, so no wave waits behind the others'.
 // The running max is only moved (and O rescaled) when a tile's max exceeds
-// it by more than 2^8, so most tiles skip the rescale.
+// it by more than 2^8, so most tiles skip the rescale. On sliding-window
+// layers the queries enter the scores as bf16 high + low parts (two S MFMAs
+// per K fragment), for error margin.
 #include <type_traits>
 
 #include "hattn_device.h"
