@@ -415,13 +415,20 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
 
   // Mask of tile t's scores. Register i of block kb holds key row
   // t*64 + kb*32 + 8*(i/4) + 4*(lane/32) + i%4 for query lane % 32.
+  // Branch-free (key_visible's short-circuit tests compiled to a branch per
+  // element): a key at distance d = pq - pk behind the query is visible iff
+  // 0 <= d < window (any d >= 0 without a window) and its row is valid; one
+  // unsigned compare covers both bounds, since a negative d turns into a
+  // value of 2^31 or more. Key positions are never negative here (kp0 >= 0).
+  const unsigned wlim = a.window > 0 ? (unsigned)a.window : 0x7fffffffu;
   auto mask_s = [&](int t, f32x16& s0, f32x16& s1) __attribute__((always_inline)) {
     const int pq = pq_first + (lane & 31);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int k0 = t * kBN + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      const bool ok0 = k0 < nk && key_visible(pq, kp0 + k0, a.window);
-      const bool ok1 = k0 + 32 < nk && key_visible(pq, kp0 + k0 + 32, a.window);
+      const int d0 = pq - (kp0 + k0);
+      const bool ok0 = ((unsigned)d0 < wlim) & (k0 < nk);
+      const bool ok1 = ((unsigned)(d0 - 32) < wlim) & (k0 + 32 < nk);
       s0[i] = ok0 ? s0[i] : -__builtin_inff();
       s1[i] = ok1 ? s1[i] : -__builtin_inff();
     }
