@@ -77,6 +77,11 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// LDS byte address of a shared-memory pointer.
+__device__ __forceinline__ uint32_t lds_u32(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Two floats to packed bf16 (low half first), rounded to nearest even by
@@ -412,6 +417,21 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
     for (int e = 0; e < 2; ++e)
       v_addr[e] = 512 * (G >> 1) + 128 * v + 16 * ((4 * e + 2 * (G & 1) + (w >> 1)) ^ (2 * v)) + 8 * (w & 1);
   }
+  // The V slots lie above 64 KiB of LDS, past the reach of a DS
+  // instruction's 16-bit offset field, so the compiler built every
+  // transposed read's address with its own v_or (64 per step). With the
+  // slot's LDS address added to v_addr once, in registers it cannot see
+  // into, the remaining constant fits the offset field. The reads still
+  // index the slot array itself (slot + (va_abs - address of slot)), so the
+  // compiler keeps telling them apart from the DMA into the other slot.
+  uint32_t va_abs[2][2];
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      va_abs[sl][e] = (uint32_t)v_addr[e] + lds_u32(sl ? v_lds1 : v_lds0);
+      asm volatile("" : "+v"(va_abs[sl][e]));
+    }
 
   // Mask of tile t's scores. Register i of block kb holds key row
   // t*64 + kb*32 + 8*(i/4) + 4*(lane/32) + i%4 for query lane % 32.
@@ -457,7 +477,8 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
         const int ks = i >> 1;
         kr[i % kRing] = *(const bf16x8*)(kslot + k_addr[ks & 3] + (i & 1) * 16384 + (ks >> 2) * 1024);
       } else {        // P.V MFMA i = tt*8 + db
-        const char* vp = vslot + v_addr[i & 1] + (i >> 3) * 8192 + ((i & 7) >> 1) * 1024;
+        const uint32_t vb = va_abs[vslot == v_lds1 ? 1 : 0][i & 1];
+        const char* vp = vslot + (vb - lds_u32(vslot)) + (i >> 3) * 8192 + ((i & 7) >> 1) * 1024;
         const s16x4 lo = lds_read_tr(vp);
         const s16x4 hi = lds_read_tr(vp + 4096);
         vr[i % kRing] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
