@@ -616,6 +616,11 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
     // matrix-core stream it is interleaved with.
     asm volatile("" : "+v"(pn[0]), "+v"(pn[1]), "+v"(pn[2]), "+v"(pn[3]), "+v"(alpha_pending), "+v"(l_i),
                  "+v"(m_i));
+    // The next tile's scores are wanted in VGPRs at the step's end: without
+    // this the compiler copies them out of the accumulation registers at the
+    // start of the next step, 32 reads in a row ahead of its barrier, and
+    // zeroes the accumulators with 32 writes per two steps.
+    asm volatile("" : "+v"(sn0), "+v"(sn1));
     if (j + 1 < nt && need_mask(t + 1)) mask_s(t + 1, sn0, sn1);
   };
   // even j: S(t) in sA, P(t) -> pA, P(t-1) in pB; odd j: the other way round
