@@ -27,9 +27,11 @@ back to back). The calls cycle over enough distinct caches that the 256 MB
 last-level cache cannot serve the KV cache.
 
 "roofline" describes the prefill attention kernel (HIP events around each of
-its launches in the timed steps), with the HBM traffic and the shader clock
-from the committed rocprofv3 counter passes when the kernel source still
-matches them. "practical_ceilings" times the library's streaming-read and
+its launches in the timed steps), with the shader clock those launches ran at
+(stamped by the kernel's workgroups through the library's profiling hook) and
+the fraction of peak at that clock, and with the HBM traffic and MFMA-busy
+fraction from the committed rocprofv3 counter passes when the kernel source
+still matches them. "practical_ceilings" times the library's streaming-read and
 MFMA probes and torch's bf16 GEMM beside the path. "cpu_baseline" times the
 fp64 oracle on the host on a bounded sample of each workload.
 
@@ -49,6 +51,7 @@ if ROOT not in sys.path:
 
 METRIC = "prefill attention TFLOP/s + decode KV GB/s (% of MI355X peak), 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+NOMINAL_SCLK_GHZ = 2.4      # the clock that peak assumes (256 CUs x 4096 flop/clk)
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = {
@@ -96,7 +99,10 @@ def counter_clock():
     """The prefill kernel's average shader clock and MFMA-busy fraction from
     the committed rocprofv3 counter pass (GRBM_GUI_ACTIVE per XCD over the
     dispatch time; SQ_VALU_MFMA_BUSY_CYCLES over the SIMD cycles), or None
-    when the summary is missing or the kernel's source has changed since."""
+    when the summary is missing or the kernel's source has changed since.
+    The profiler serialises those launches, with idle time between them, so
+    their clock can differ from that of back-to-back launches
+    (shader_clock_GHz in the roofline)."""
     p = os.path.join(PROFILES, "prefill_mfma_counters.json")
     if not os.path.exists(p):
         return None
@@ -450,6 +456,7 @@ def run(args):
     ms = time_calls(torch, prefill, args.steps, 0)
     hb.hattn_profile_enable(False)
     n, attn_total = hb.hattn_profile_read(hb.PROFILE_PREFILL)
+    sclk = hb.hattn_profile_read_clock()  # the same timed launches
     attn_ms = attn_total / max(n, 1)
     log(f"prefill: {ms:.4f} ms/call, attention kernel {attn_ms:.4f} ms over {n} launches, "
         f"{flops / ms / 1e9:.1f} TFLOP/s per call")
@@ -460,7 +467,13 @@ def run(args):
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
         "traffic": counter_traffic("prefill_full_s8192"),
         "kernel": "prefill_attn_kernel", "flop_per_launch": flops, "avg_launch_ms": round(attn_ms, 5),
-        "launches_timed": n, "clock_from_counters": counter_clock(),
+        "launches_timed": n,
+        # shader clock of the timed launches (per workgroup, s_memtime against
+        # the fixed-rate s_memrealtime), and the fraction of the bf16 peak at
+        # that clock (the published peak assumes 2.4 GHz)
+        "shader_clock_GHz": round(sclk, 3),
+        "frac_at_shader_clock": round(achieved / (PEAK_BF16_TFLOPS * sclk / NOMINAL_SCLK_GHZ), 4) if sclk > 0 else None,
+        "clock_from_counters": counter_clock(),
     }
     del inp, cache, out, ws
     torch.cuda.empty_cache()

@@ -113,6 +113,7 @@ _SIGS = {
     "hattn_debug_mfma_probe": (ctypes.c_int, [_I, _I, _P, _P]),
     "hattn_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "hattn_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]),
+    "hattn_profile_read_clock": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double)]),
 }
 PROFILE_PREFILL, PROFILE_DECODE = 0, 1
 
@@ -487,6 +488,14 @@ def hattn_profile_read(kind):
     ms = ctypes.c_double()
     _check("hattn_profile_read", lib().hattn_profile_read(kind, ctypes.byref(n), ctypes.byref(ms)))
     return int(n.value), float(ms.value)
+
+
+def hattn_profile_read_clock():
+    """Average shader clock (GHz) of the prefill attention kernels profiled
+    since the last read (0.0 when none were)."""
+    g = ctypes.c_double()
+    _check("hattn_profile_read_clock", lib().hattn_profile_read_clock(ctypes.byref(g)))
+    return float(g.value)
 
 
 def debug_read_probe(buf, blocks, sink):

@@ -368,6 +368,7 @@ int prefill_packed(const hattn_layer_desc* desc, const void* q, const void* k, c
   aa.r = r;
   aa.gate_act = desc->gate_act;
   aa.q_tiles = (max_len + kPrefillBlockQ - 1) / kPrefillBlockQ;
+  if (g_profile && prefill_clock_acc(&aa.clock_acc) != hipSuccess) aa.clock_acc = nullptr;
   hipEvent_t prof = profile_begin(HATTN_PROFILE_PREFILL, stream);
   e = launch_prefill_attn(aa, stream);
   profile_end(prof, stream);
@@ -609,6 +610,27 @@ int hattn_decode_static(const hattn_layer_desc* desc, const void* q, const void*
 
 int hattn_profile_enable(int enable) {
   g_profile = enable != 0;
+  if (g_profile) {  // start the current GPU's clock sums from zero
+    unsigned long long* acc = nullptr;
+    if (prefill_clock_acc(&acc) != hipSuccess || hipMemset(acc, 0, 2 * sizeof(unsigned long long)) != hipSuccess)
+      return HATTN_ERR_LAUNCH;
+  }
+  return HATTN_OK;
+}
+
+int hattn_profile_read_clock(double* shader_ghz) {
+  if (!shader_ghz) return HATTN_ERR_NULL;
+  *shader_ghz = 0.0;
+  unsigned long long* acc = nullptr;
+  unsigned long long h[2] = {0, 0};
+  int dev = 0, khz = 0;
+  if (prefill_clock_acc(&acc) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+      hipMemcpy(h, acc, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemset(acc, 0, sizeof(h)) != hipSuccess || hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+    return HATTN_ERR_LAUNCH;
+  // shader ticks per real-time tick, times the real-time counter's rate
+  if (h[1] > 0 && khz > 0) *shader_ghz = (double)h[0] / (double)h[1] * (double)khz * 1e-6;
   return HATTN_OK;
 }
 

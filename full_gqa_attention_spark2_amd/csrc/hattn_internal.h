@@ -84,6 +84,9 @@ struct PrefillAttnArgs {
   int n_keys[kMaxPrefillBatch];    // valid key rows
   int tok0[kMaxPrefillBatch];      // packed row of query 0
   int len[kMaxPrefillBatch];       // queries of sequence b
+  // When not null (profiling on): each workgroup adds its elapsed shader
+  // clock ticks to [0] and real-time counter ticks to [1].
+  unsigned long long* clock_acc;
 };
 
 struct DecodeArgs {
@@ -188,6 +191,9 @@ size_t decode_workspace_bytes(const hattn_layer_desc* desc, const hattn_kv_cache
 hipError_t launch_prefill_prep(const PrefillPrepArgs& a, hipStream_t s);
 hipError_t launch_ring_to_stage(const RingCopyArgs& a, hipStream_t s);
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s);
+// Device address of the current device's prefill clock accumulators (two
+// unsigned 64-bit counters, see PrefillAttnArgs::clock_acc).
+hipError_t prefill_clock_acc(unsigned long long** ptr);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 // Device address of the current device's static decode scratch
 // (HATTN_DECODE_STATIC_SCRATCH_BYTES), looked up on first use per device.

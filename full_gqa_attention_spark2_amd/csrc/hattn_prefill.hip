@@ -30,8 +30,16 @@
 // per K fragment), for error margin.
 #include <type_traits>
 
+#include <mutex>
+
 #include "hattn_device.h"
 #include "hattn_internal.h"
+
+// Clock accumulators of the profiling hook (sums of shader clock ticks and of
+// real-time counter ticks over the profiled workgroups), one pair per GPU.
+// Host code uses their device address from prefill_clock_acc(), never the
+// symbol itself.
+static __device__ unsigned long long clock_acc[2];
 
 namespace hattn {
 
@@ -187,6 +195,13 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   const int kvh = r2 % a.Hkv;
   const int len = a.len[b];
   if (qt * kBM >= len) return;
+  // Profiling: the workgroup's start on the shader clock and on the
+  // fixed-rate real-time counter, parked in LDS until its end.
+  __shared__ unsigned long long clk_start[2];
+  if (a.clock_acc && threadIdx.x == 0) {
+    clk_start[0] = __builtin_amdgcn_s_memtime();
+    clk_start[1] = __builtin_amdgcn_s_memrealtime();
+  }
   const size_t tok0 = (size_t)a.tok0[b];  // packed row of the sequence's query 0
 
   const int lane = threadIdx.x & 63;
@@ -671,6 +686,30 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
         *(uint4*)(a.out + ((tok0 + q0 + r) * a.Hq + h) * kHeadDim + (lane & 31) * 8) = v;
     }
   }
+  if (a.clock_acc && threadIdx.x == 0) {
+    atomicAdd(&a.clock_acc[0], __builtin_amdgcn_s_memtime() - clk_start[0]);
+    atomicAdd(&a.clock_acc[1], __builtin_amdgcn_s_memrealtime() - clk_start[1]);
+  }
+}
+
+hipError_t prefill_clock_acc(unsigned long long** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static unsigned long long* addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(clock_acc));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = (unsigned long long*)p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s) {

@@ -362,6 +362,16 @@ typedef enum { HATTN_PROFILE_PREFILL = 0, HATTN_PROFILE_DECODE = 1 } hattn_profi
 int hattn_profile_enable(int enable);
 int hattn_profile_read(int kind, int64_t* count, double* total_ms);
 
+/* The shader clock the prefill attention kernel ran at while profiling was
+ * enabled: each workgroup of each profiled hattn_prefill adds its elapsed
+ * shader clock ticks (s_memtime) and real-time counter ticks
+ * (s_memrealtime) to two counters on the GPU; this returns their ratio times
+ * the real-time counter's rate (hipDeviceAttributeWallClockRate), in GHz,
+ * for the current device, and sets both counters back to zero
+ * (hattn_profile_enable(1) zeroes them too). 0 when nothing was recorded.
+ * Synchronises the device. Errors: HATTN_ERR_NULL, HATTN_ERR_LAUNCH. */
+int hattn_profile_read_clock(double* shader_ghz);
+
 /* Name of a status code (static string). */
 const char* hattn_status_string(int status);
 

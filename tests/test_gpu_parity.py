@@ -989,6 +989,29 @@ def test_profiling_hook_counts_and_times_kernel_sections():
     assert hb.hattn_profile_read(hb.PROFILE_PREFILL) == (0, 0.0)
 
 
+def test_profiling_hook_reads_the_prefill_shader_clock():
+    # the clock the bench reports for its timed launches: a plausible MI355X
+    # shader clock while profiling, reset by each read, nothing recorded with
+    # profiling off; the stamps change no output bit
+    desc = hb.layer_desc("full")
+    inp = to_dev(synth.prefill_inputs(1, 512, 16, 4, seed=53))
+    cache = hb.KVCache.empty(1, 4, 512, "linear")
+    plain = hb.hattn_prefill(desc, inp["q"], inp["k"], inp["v"], inp["gate"], [0], cache)
+    hb.hattn_profile_enable(True)
+    try:
+        stamped = hb.hattn_prefill(desc, inp["q"], inp["k"], inp["v"], inp["gate"], [0], cache)
+        ghz = hb.hattn_profile_read_clock()
+    finally:
+        hb.hattn_profile_enable(False)
+    hb.hattn_profile_read(hb.PROFILE_PREFILL)
+    print(f"prefill shader clock while profiled: {ghz:.3f} GHz", flush=True)
+    assert 0.3 < ghz < 3.5
+    assert torch.equal(plain, stamped)
+    assert hb.hattn_profile_read_clock() == 0.0
+    hb.hattn_prefill(desc, inp["q"], inp["k"], inp["v"], inp["gate"], [0], cache)
+    assert hb.hattn_profile_read_clock() == 0.0
+
+
 # ------------------------------------------------------------------ chunked prefill, 1.7B shape
 @pytest.mark.parametrize("layer", ["full", "sliding"])
 def test_chunked_prefill_1p7b_shape_sampled(layer):
