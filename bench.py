@@ -199,7 +199,9 @@ def ceilings(torch, hb, dev, steps=5):
     back to back): the library's plain streaming-read probe over 4 GiB and
     over 8 distinct 128 MiB buffers in turn (the sliding decode's size and
     grid), back-to-back bf16 MFMA on every CU (with the shader clock over
-    it), and torch's bf16 GEMM of 8192^3 (hipBLASLt)."""
+    it), the LDS read rate of the prefill kernel's fragment reads (alone and
+    mixed with its MFMAs, on the shader clock) and torch's bf16 GEMM of
+    8192^3 (hipBLASLt)."""
     res = {}
     sink = torch.zeros(8192, dtype=torch.int32, device=dev)
     big = torch.empty(1 << 30, dtype=torch.int32, device=dev).random_()  # 4 GiB
@@ -232,6 +234,21 @@ def ceilings(torch, hb, dev, steps=5):
     # rate implies (1,024 SIMDs x 1,024 flop per cycle)
     res["mfma_bf16_32x32x16_probe"] = {"ms": round(ms, 4), "TFLOP_per_s": round(tf, 1),
                                        "implied_sclk_GHz": round(tf * 1e12 / (1024 * 1024) / 1e9, 3)}
+    # LDS: bytes per shader clock and CU for the prefill kernel's fragment
+    # reads, and the prefill step's reads mixed with its MFMAs (cycles per
+    # MFMA; 32 when the matrix core never waits), one block per CU
+    out = torch.zeros(256, 2, dtype=torch.int64, device=dev)
+    lds = {}
+    for mode, name, iters_l, per_round in ((0, "ds_read_b128", 4000, 32768), (1, "ds_read_b64_tr_b16", 4000, 16384),
+                                           (2, "prefill_step_reads_with_mfma", 500, None)):
+        hb.debug_lds_probe(mode, 256, iters_l, out)
+        torch.cuda.synchronize()
+        ticks = float(out[:, 0].double().median())
+        if per_round:
+            lds[name] = {"B_per_clock_per_CU": round(iters_l * per_round / ticks, 1), "waves_per_CU": 4}
+        else:
+            lds[name] = {"cycles_per_mfma": round(ticks / (iters_l * 64), 2), "reads_per_mfma": 1.5, "waves_per_CU": 4}
+    res["lds_probe"] = lds
     a = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
     b = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
     ms = time_calls(torch, lambda: torch.mm(a, b), steps, 2)

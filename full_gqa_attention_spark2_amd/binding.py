@@ -111,6 +111,7 @@ _SIGS = {
     "hattn_debug_index_probe": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _I, _I, _I, _I, _P, _P, _P, _P]),
     "hattn_debug_read_probe": (ctypes.c_int, [_P, ctypes.c_size_t, _I, _P, _P]),
     "hattn_debug_mfma_probe": (ctypes.c_int, [_I, _I, _P, _P]),
+    "hattn_debug_lds_probe": (ctypes.c_int, [_I, _I, _I, _P, _P]),
     "hattn_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "hattn_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]),
     "hattn_profile_read_clock": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double)]),
@@ -507,3 +508,10 @@ def debug_read_probe(buf, blocks, sink):
 def debug_mfma_probe(blocks, iters, sink):
     """Back-to-back bf16 MFMA 32x32x16 in `blocks` four-wave blocks."""
     _check("hattn_debug_mfma_probe", lib().hattn_debug_mfma_probe(blocks, iters, _ptr(sink), _stream(sink.device)))
+
+
+def debug_lds_probe(mode, blocks, iters, out):
+    """LDS fragment reads (mode 0 b128, 1 transposed b64, 2 mixed with MFMA) in
+    `blocks` four-wave blocks; out: int64 device tensor [blocks][2], [b][0] =
+    elapsed shader clock ticks of block b."""
+    _check("hattn_debug_lds_probe", lib().hattn_debug_lds_probe(mode, blocks, iters, _ptr(out), _stream(out.device)))

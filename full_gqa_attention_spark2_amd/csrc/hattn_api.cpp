@@ -671,6 +671,13 @@ int hattn_debug_mfma_probe(int32_t blocks, int32_t iters, float* sink, hipStream
   return from_hip(launch_mfma_probe(blocks, iters, sink, stream));
 }
 
+int hattn_debug_lds_probe(int32_t mode, int32_t blocks, int32_t iters, uint64_t* out, hipStream_t stream) {
+  if (mode < 0 || mode > 2 || blocks < 1 || iters < 1) return HATTN_ERR_SHAPE;
+  if (!out) return HATTN_ERR_NULL;
+  if ((uintptr_t)out & 7u) return HATTN_ERR_ALIGN;
+  return from_hip(launch_lds_probe(mode, blocks, iters, (unsigned long long*)out, stream));
+}
+
 int hattn_debug_index_probe(const hattn_layer_desc* desc, int32_t kv_kind, int32_t capacity,
                             int32_t q_pos0, int32_t n_q, uint8_t* mask, int32_t* key_pos,
                             int32_t* slot, hipStream_t stream) {

@@ -208,6 +208,7 @@ bool skinny_gemm_fits(int N, int K, int T, long long lda, long long ldd, const v
 hipError_t launch_skinny_gemm(const SkinnyGemmArgs& g, hipStream_t s);
 hipError_t launch_read_probe(const void* buf, size_t bytes, int blocks, uint32_t* sink, hipStream_t s);
 hipError_t launch_mfma_probe(int blocks, int iters, float* sink, hipStream_t s);
+hipError_t launch_lds_probe(int mode, int blocks, int iters, unsigned long long* out, hipStream_t s);
 hipError_t launch_residual_add(const float* x, const uint16_t* y, float* out, long long n, hipStream_t s);
 
 }  // namespace hattn

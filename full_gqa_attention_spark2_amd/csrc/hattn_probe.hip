@@ -4,7 +4,11 @@
 //     flight per thread), the practical HBM read rate at a given size;
 //   - mfma_probe_kernel: back-to-back bf16 MFMA 32x32x16 on pseudo-random
 //     operands, the practical matrix-core rate under full load (the clock
-//     drops under it).
+//     drops under it);
+//   - lds_probe_kernel: LDS fragment reads as the prefill kernel issues them
+//     (b128, transposed b64, and their mix with MFMAs), timed on the shader
+//     clock, so the LDS rate per CU and cycle can be read beside the MFMA
+//     rate.
 // None of them is on the attention path.
 #include "hattn_device.h"
 #include "hattn_internal.h"
@@ -63,7 +67,90 @@ __global__ __launch_bounds__(256, 1) void mfma_probe_kernel(int iters, float* si
   if (lane == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = x;
 }
 
+// Four waves per block, one block per CU (64 KiB of LDS). Each wave reads
+// its own 16 KiB quarter. Mode 0: 8 ds_read_b128 in flight per wave and
+// round (1 KiB each); mode 1: 8 ds_read_b64_tr_b16 (512 B each); mode 2:
+// the prefill step's stream without its softmax, 64 bf16 MFMA 32x32x16 per
+// round with one b128 read ahead of every S element and two transposed reads
+// ahead of every P.V element (32 + 64 reads), three elements ahead. out[2b]:
+// wave 0's elapsed shader clock ticks (s_memtime); out[2b + 1] keeps the
+// reads alive.
+typedef short s16x4p __attribute__((ext_vector_type(4)));
+template <int Mode>
+__global__ __launch_bounds__(256, 1) void lds_probe_kernel(int iters, unsigned long long* out) {
+  __shared__ __attribute__((aligned(1024))) char lds[65536];
+  for (int i = threadIdx.x; i < 65536 / 4; i += 256) {
+    uint32_t x = (uint32_t)i * 2654435761u + 12345u;
+    x ^= x >> 13;
+    ((uint32_t*)lds)[i] = (x & 0x807f807fu) | 0x3c003c00u;  // bf16 pairs in [-2, 2)
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const char* base = lds + (threadIdx.x >> 6) * 16384;
+  auto tr = [](const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4p*)(p));
+  };
+  f32x16 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+  bf16x8 bq;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) bq[j] = (__bf16)(0.001f * (lane + j));
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+    // a fresh address each round, so nothing is hoisted or merged; every
+    // read stays inside the wave's quarter (modes 0 and 1: b + 8 KiB at
+    // most; mode 2: b + 12 KiB, with b at most 4 KiB into the quarter)
+    int boff = (it & 1) * (Mode == 2 ? 4096 : 8192);
+    asm volatile("" : "+v"(boff));
+    const char* b = base + boff;
+    if constexpr (Mode == 0) {
+      u32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *(const u32x4*)(b + u * 1024 + lane * 16);
+      asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]));
+    } else if constexpr (Mode == 1) {
+      s16x4p v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = tr(b + u * 1024 + lane * 8);
+      asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]));
+    } else {
+      bf16x8 r[4];
+      auto rd = [&](int n) __attribute__((always_inline)) {
+        if (n & 1) {  // within b .. b + 4 KiB
+          const s16x4p lo = tr(b + (n & 7) * 512 + lane * 8);
+          const s16x4p hi = tr(b + (n & 7) * 512 + 256 + lane * 8);
+          r[n & 3] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {  // within b + 8 KiB .. b + 12 KiB
+          r[n & 3] = *(const bf16x8*)(b + 8192 + (n & 6) * 512 + lane * 16);
+        }
+      };
+      rd(0);
+      rd(1);
+      rd(2);
+#pragma unroll
+      for (int n = 0; n < 64; ++n) {
+        if (n + 3 < 64) rd(n + 3);
+        acc[n & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r[n & 3], bq, acc[n & 3], 0, 0, 0);
+      }
+    }
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  float x = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x += acc[i][lane & 15];
+  if (threadIdx.x == 0) out[2 * blockIdx.x] = t1 - t0;
+  if (x == 1234.5f) out[2 * blockIdx.x + 1] = (unsigned long long)__float_as_uint(x);
+}
+
 }  // namespace
+
+hipError_t launch_lds_probe(int mode, int blocks, int iters, unsigned long long* out, hipStream_t s) {
+  if (mode == 0) hipLaunchKernelGGL(lds_probe_kernel<0>, dim3(blocks), dim3(256), 0, s, iters, out);
+  else if (mode == 1) hipLaunchKernelGGL(lds_probe_kernel<1>, dim3(blocks), dim3(256), 0, s, iters, out);
+  else hipLaunchKernelGGL(lds_probe_kernel<2>, dim3(blocks), dim3(256), 0, s, iters, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_read_probe(const void* buf, size_t bytes, int blocks, uint32_t* sink, hipStream_t s) {
   hipLaunchKernelGGL(read_probe_kernel, dim3(blocks), dim3(256), 0, s, (const u32x4*)buf, bytes / 16, sink);

@@ -397,11 +397,22 @@ int hattn_debug_index_probe(const hattn_layer_desc* desc, int32_t kv_kind,
  * hattn_debug_mfma_probe: `blocks` blocks of four waves each run `iters`
  *   rounds of 8 independent bf16 MFMA 32x32x16 (262,144 flop per wave and
  *   round) on pseudo-random operands; sink: device float [blocks][4].
+ * hattn_debug_lds_probe: `blocks` blocks of four waves (64 KiB of LDS, one
+ *   per CU) each run `iters` rounds of LDS fragment reads as the prefill
+ *   kernel issues them; mode 0: 8 ds_read_b128 per wave and round (32 KiB
+ *   per block and round), mode 1: 8 ds_read_b64_tr_b16 (16 KiB), mode 2:
+ *   64 bf16 MFMA 32x32x16 per wave and round with 32 b128 and 64 transposed
+ *   reads among them (the prefill step without its softmax and tile loads).
+ *   out: device uint64 [blocks][2]; out[2b] receives block b's elapsed
+ *   shader clock ticks (s_memtime of its first wave), out[2b + 1] is written
+ *   only in a case the data never meets.
  * Errors: HATTN_ERR_SHAPE, _NULL, _ALIGN as for the other entry points. */
 int hattn_debug_read_probe(const void* buf, size_t bytes, int32_t blocks,
                            uint32_t* sink, hipStream_t stream);
 int hattn_debug_mfma_probe(int32_t blocks, int32_t iters, float* sink,
                            hipStream_t stream);
+int hattn_debug_lds_probe(int32_t mode, int32_t blocks, int32_t iters,
+                          uint64_t* out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

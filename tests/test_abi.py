@@ -311,3 +311,18 @@ def test_decode_static_validates_before_using_its_scratch(L):
     assert st(fu, lin, max_pos=1 << 20) == -7
     assert st(fu, lin, pos=0) == -1
     assert st(fu, lin, max_pos=(1 << 20) - 1) == -10      # valid: reaches the launch
+
+
+@fake_pointers
+def test_measurement_probes_reject_bad_arguments(L):
+    # modes, counts and the output pointer are checked before any launch
+    lds = L.hattn_debug_lds_probe
+    assert lds(3, 1, 1, FAKE, None) == -2
+    assert lds(-1, 1, 1, FAKE, None) == -2
+    assert lds(0, 0, 1, FAKE, None) == -2
+    assert lds(0, 1, 0, FAKE, None) == -2
+    assert lds(0, 1, 1, None, None) == -1
+    assert lds(0, 1, 1, FAKE + 4, None) == -9
+    assert L.hattn_debug_mfma_probe(0, 1, FAKE, None) == -2
+    assert L.hattn_debug_mfma_probe(1, 1, None, None) == -1
+    assert L.hattn_debug_read_probe(FAKE, 24, 1, FAKE, None) == -2

@@ -989,6 +989,27 @@ def test_profiling_hook_counts_and_times_kernel_sections():
     assert hb.hattn_profile_read(hb.PROFILE_PREFILL) == (0, 0.0)
 
 
+def test_lds_probe_reports_plausible_rates():
+    # the bench's LDS ceiling: every block records its shader clock ticks;
+    # reads per clock and cycles per MFMA within what a CU can do
+    out = torch.zeros(256, 2, dtype=torch.int64, device=DEV)
+    for mode, iters, per_round in ((0, 200, 32768), (1, 200, 16384), (2, 50, None)):
+        out.zero_()
+        hb.debug_lds_probe(mode, 256, iters, out)
+        torch.cuda.synchronize()
+        ticks = out[:, 0].double()
+        assert bool((ticks > 0).all()), mode
+        med = float(ticks.median())
+        if per_round:
+            bpc = iters * per_round / med
+            print(f"LDS probe mode {mode}: {bpc:.1f} B per clock per CU", flush=True)
+            assert 16.0 < bpc <= 1024.0
+        else:
+            cpm = med / (iters * 64)
+            print(f"LDS probe mode 2: {cpm:.2f} cycles per MFMA", flush=True)
+            assert 16.0 <= cpm < 400.0
+
+
 def test_profiling_hook_reads_the_prefill_shader_clock():
     # the clock the bench reports for its timed launches: a plausible MI355X
     # shader clock while profiling, reset by each read, nothing recorded with
