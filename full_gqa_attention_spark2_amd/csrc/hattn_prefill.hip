@@ -618,8 +618,11 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
     // O holds P.V up to tile t-2 plus (below) tile t-1, all relative to the
     // max before softmax(t-1); a max move found by softmax(t-1) is applied
     // here, before P(t-1).V(t-1) is added, so no branch on the max sits
-    // inside the stream.
-    if (rescale_pending) rescale_o(alpha_pending);
+    // inside the stream. In the first P.V step (j = 1) O is still zero while
+    // the first softmax always moves the max off its start value: that
+    // rescale would only multiply zeros (the running sum is rescaled inside
+    // the softmax).
+    if (rescale_pending && j > 1) rescale_o(alpha_pending);
     mma_stream(mode, kn, vp, sn0, sn1, pp, [&](int e) __attribute__((always_inline)) {
         if (e % kLoadSpacing == 0 && e < 4 * kLoadSpacing && wave == e / kLoadSpacing) load_tiles();
     });
@@ -644,10 +647,10 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
     step(ModeSPv{}, j, k_lds0, v_lds0, k_lds1, v_lds1, sB0, sB1, sA0, sA1, pA, pB);
     if (j + 1 < nt) step(ModeSPv{}, j + 1, k_lds1, v_lds1, k_lds0, v_lds0, sA0, sA1, sB0, sB1, pB, pA);
   }
-  // P.V of the last tile
+  // P.V of the last tile (with a single tile, O is still zero: no rescale)
   wait_loads();
   __syncthreads();
-  if (rescale_pending) rescale_o(alpha_pending);
+  if (rescale_pending && nt > 1) rescale_o(alpha_pending);
   if ((nt - 1) & 1) {
     mma_stream(ModePv{}, k_lds0, v_lds1, sA0, sA1, pB, [](int) {});
     issue_order<kStreamPv, 0, kSplitQ>();
