@@ -28,9 +28,8 @@
 // it by more than 2^8, so most tiles skip the rescale. On sliding-window
 // layers the queries enter the scores as bf16 high + low parts (two S MFMAs
 // per K fragment), for error margin.
-#include <type_traits>
-
 #include <mutex>
+#include <type_traits>
 
 #include "hattn_device.h"
 #include "hattn_internal.h"
