@@ -305,15 +305,48 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
     // the rotation runs on registers.
     auto rope_fast = [&](auto np) __attribute__((always_inline)) {
       constexpr int NP = decltype(np)::value;  // rotated fragment pairs (ks, ks + NP)
+      // The cos/sin rows of the block's 32 queries (128 NP bytes each) are
+      // the same for all four waves. They come into the free V slot v_lds1
+      // by LDS DMA, whole 128-byte lines per instruction (NP instructions
+      // per wave), instead of 4 NP loads per lane that each touch 32 rows.
+      // Row i (query q0 + i, clamped like qr) keeps its 16-byte chunk c at
+      // position c ^ (i & 7), which spreads the reads below over the banks.
+      constexpr int kRowBytes = 128 * NP;
+      {
+        const __amdgpu_buffer_rsrc_t trs =
+            slab_rsrc(a.table + tok0 * (size_t)half, (uint32_t)len * (uint32_t)kRowBytes);
+#pragma unroll
+        for (int u = 0; u < NP; ++u) {
+          const uint32_t off = (uint32_t)(wave * NP + u) * 1024u + 16u * (uint32_t)lane;  // byte in the copy
+          const int i = (int)(off / kRowBytes);
+          const uint32_t pos = (off % kRowBytes) / 16u;
+          const uint32_t src = (uint32_t)min(q0 + i, len - 1) * kRowBytes + 16u * (pos ^ (uint32_t)(i & 7));
+          load_lds16(trs, src, 0, v_lds1 + (wave * NP + u) * 1024);
+        }
+      }
+      asm volatile("" ::: "memory");  // issue order: table rows, then queries, then first tiles
       uint4 raw[16];
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) raw[ks] = *(const uint4*)(qp + ks * 16 + (lane >> 5) * 8);
-      uint4 cs[NP][4];  // (cos, sin) of table entries 16p + 8(lane/32) + 0..7
-#pragma unroll
-      for (int pp = 0; pp < NP; ++pp)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) cs[pp][u] = *(const uint4*)(tp + pp * 16 + (lane >> 5) * 8 + 2 * u);
+      asm volatile("" ::: "memory");
       load_first_tiles();
+      // This wave's table rows have landed once at most the 16 query loads
+      // and the first tiles' 8 or 16 loads are outstanding; after the
+      // barrier, every wave's have. (A bare s_barrier: __syncthreads would
+      // also wait for the queries and the tiles.)
+      if (nt > 1) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      uint4 cs[NP][4];  // (cos, sin) of table entries 16p + 8(lane/32) + 0..7
+      {
+        const int i = qr - q0;
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            cs[pp][u] = *(const uint4*)(v_lds1 + i * kRowBytes + 16 * ((8 * pp + 4 * (lane >> 5) + u) ^ (i & 7)));
+      }
       // Rows past the sequence's end hold the last row's queries (qr is
       // clamped): their columns repeat a column of the same wave, so they
       // change none of its decisions, and their outputs are not stored.
@@ -340,8 +373,10 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
           const uint4 w = cs[pp][j >> 1];
           const float2 t = (j & 1) ? make_float2(__uint_as_float(w.z), __uint_as_float(w.w))
                                    : make_float2(__uint_as_float(w.x), __uint_as_float(w.y));
-          ra[j] = xa[j] * t.x - xb[j] * t.y;
-          rb[j] = xb[j] * t.x + xa[j] * t.y;
+          // explicit fused multiply-adds: the rounding does not depend on
+          // how the compiler would contract the expression
+          ra[j] = __builtin_fmaf(xa[j], t.x, -(xb[j] * t.y));
+          rb[j] = __builtin_fmaf(xb[j], t.x, xa[j] * t.y);
         }
         put(pp, ra);
         put(pp + NP, rb);
@@ -370,7 +405,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const float2 t = cs[j];
-            x[j] = first ? x[j] * t.x - xp[j] * t.y : x[j] * t.x + xp[j] * t.y;
+            x[j] = first ? __builtin_fmaf(x[j], t.x, -(xp[j] * t.y)) : __builtin_fmaf(x[j], t.x, xp[j] * t.y);
           }
         }
         bf16x8 v;
