@@ -313,14 +313,16 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
       // position c ^ (i & 7), which spreads the reads below over the banks.
       constexpr int kRowBytes = 128 * NP;
       {
+        // a resource over the block's own rows (nq of them), so every offset
+        // stays below 32 KiB whatever the sequence's length
         const __amdgpu_buffer_rsrc_t trs =
-            slab_rsrc(a.table + tok0 * (size_t)half, (uint32_t)len * (uint32_t)kRowBytes);
+            slab_rsrc(a.table + (tok0 + q0) * (size_t)half, (uint32_t)nq * (uint32_t)kRowBytes);
 #pragma unroll
         for (int u = 0; u < NP; ++u) {
           const uint32_t off = (uint32_t)(wave * NP + u) * 1024u + 16u * (uint32_t)lane;  // byte in the copy
           const int i = (int)(off / kRowBytes);
           const uint32_t pos = (off % kRowBytes) / 16u;
-          const uint32_t src = (uint32_t)min(q0 + i, len - 1) * kRowBytes + 16u * (pos ^ (uint32_t)(i & 7));
+          const uint32_t src = (uint32_t)min(i, nq - 1) * kRowBytes + 16u * (pos ^ (uint32_t)(i & 7));
           load_lds16(trs, src, 0, v_lds1 + (wave * NP + u) * 1024);
         }
       }
