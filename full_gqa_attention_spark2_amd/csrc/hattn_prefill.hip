@@ -71,13 +71,20 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, uint32_t v
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds, 16, voff, soff, 0, 0);
 }
 
+// Larger of two scores. IEEE maximum (a NaN operand gives NaN, where fmaxf
+// would return the other operand); the two agree on the finite and -inf
+// values the softmax sees. It compiles to v_maximum3_f32 chains, while
+// fmaxf on values the compiler cannot see into (the pinned scores) needs a
+// canonicalising v_max per operand first.
+__device__ __forceinline__ float max_f(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Max and sum of a value over the lane pair (l, l ^ 32), by a VALU lane
 // swap (no LDS traffic). After the swap of x with itself, lanes below 32
 // hold (x[l], x[l + 32]) and the others (x[l - 32], x[l]): the pair in the
 // same order on both lanes.
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_f(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -566,13 +573,13 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
     // with the matrix-core stream without stalling it
     float t16[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) t16[i] = fmaxf(s0[i], s1[i]);
+    for (int i = 0; i < 16; ++i) t16[i] = max_f(s0[i], s1[i]);
 #pragma unroll
     for (int w = 8; w >= 1; w >>= 1)
 #pragma unroll
-      for (int i = 0; i < w; ++i) t16[i] = fmaxf(t16[i], t16[i + w]);
+      for (int i = 0; i < w; ++i) t16[i] = max_f(t16[i], t16[i + w]);
     const float mx = pair_max(t16[0]) * kScoreScale;
-    const float m_new = fmaxf(m_i, mx);
+    const float m_new = max_f(m_i, mx);
     const bool rescale = __any(m_new > m_i + kRescaleSlack);
     const float m_use = rescale ? m_new : m_i;
     alpha = fast_exp2(m_i - m_use);
