@@ -136,6 +136,15 @@ constexpr int stream_reads(int mode, int e) {  // LDS reads feeding element e
   return mode == kStreamS ? 1 : mode == kStreamPv ? 2 : ((e & 1) ? 2 : 1);
 }
 
+// f(integral_constant<int, I>) for I = B .. E-1, expanded at compile time.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // Scheduling-group barriers for one stream, in issue order: the reads of
 // the first `ahead` elements, then per element one MFMA, the reads of
 // element e + ahead and up to kValu VALU / transcendental instructions (the
@@ -144,16 +153,17 @@ constexpr int stream_reads(int mode, int e) {  // LDS reads feeding element e
 // With split queries an S element is two MFMAs (the queries' high and low
 // bf16 parts against the same K fragment).
 constexpr int kSoftmaxValuPerMfma = 3;
+constexpr int kSoftmaxValuPerMfmaEarly = 4;  // in the blocks between the load branches
 constexpr int kSgMfma = 0x008, kSgDsRead = 0x100, kSgValu = 0x002 | 0x400;
 constexpr bool stream_is_s(int mode, int e) { return mode == kStreamS || (mode == kStreamSPv && (e & 1) == 0); }
-template <int Mode, int E, int Valu, bool kSplitQ>
+template <int Mode, int E, int End, int Valu, bool kSplitQ>
 __device__ __forceinline__ void issue_order_tail() {
-  if constexpr (E < stream_length(Mode)) {
+  if constexpr (E < End) {
     __builtin_amdgcn_sched_group_barrier(kSgMfma, (kSplitQ && stream_is_s(Mode, E)) ? 2 : 1, 0);
     if constexpr (E + stream_ahead(Mode) < stream_length(Mode))
       __builtin_amdgcn_sched_group_barrier(kSgDsRead, stream_reads(Mode, E + stream_ahead(Mode)), 0);
     if constexpr (Valu > 0) __builtin_amdgcn_sched_group_barrier(kSgValu, Valu, 0);
-    issue_order_tail<Mode, E + 1, Valu, kSplitQ>();
+    issue_order_tail<Mode, E + 1, End, Valu, kSplitQ>();
   }
 }
 template <int Mode, int E, int Acc>
@@ -167,7 +177,13 @@ struct StreamHead<Mode, 0, Acc> {
 template <int Mode, int Valu, bool kSplitQ>
 __device__ __forceinline__ void issue_order() {
   __builtin_amdgcn_sched_group_barrier(kSgDsRead, StreamHead<Mode, stream_ahead(Mode), 0>::value, 0);
-  issue_order_tail<Mode, 0, Valu, kSplitQ>();
+  issue_order_tail<Mode, 0, stream_length(Mode), Valu, kSplitQ>();
+}
+// The same for the elements E .. E + kLoadSpacing - 1 alone: the basic block
+// between two waves' tile-load branches (their reads ahead included).
+template <int Mode, int E, int Valu, bool kSplitQ>
+__device__ __forceinline__ void issue_order_block() {
+  issue_order_tail<Mode, E, E + kLoadSpacing, Valu, kSplitQ>();
 }
 
 }  // namespace
@@ -527,8 +543,8 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
     constexpr int kAhead = stream_ahead(decltype(mode)::value);
     bf16x8 kr[kRing];
     s16x8 vr[kRing];
-    auto is_s = [](int e) { return kS && (!kP || (e & 1) == 0); };
-    auto index = [](int e) { return (kS && kP) ? e >> 1 : e; };
+    auto is_s = [](int e) constexpr { return kS && (!kP || (e & 1) == 0); };
+    auto index = [](int e) constexpr { return (kS && kP) ? e >> 1 : e; };
     auto issue = [&](int e) __attribute__((always_inline)) {
       const int i = index(e);
       if (is_s(e)) {  // S MFMA i: k-step i/2, key block i%2
@@ -548,12 +564,15 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
     }
 #pragma unroll
     for (int e = 0; e < kAhead; ++e) issue(e);
-#pragma unroll
-    for (int e = 0; e < kN; ++e) {
-      before(e);  // work placed ahead of element e (the tile loads)
-      if (e + kAhead < kN) issue(e + kAhead);
-      const int i = index(e);
-      if (is_s(e)) {
+    // Expanded at compile time (the hook sees each element index as a
+    // constant): a plain unrolled loop stops being unrolled once the hooks
+    // carry the softmax parts.
+    static_for<0, kN>([&](auto ec) __attribute__((always_inline)) {
+      constexpr int e = decltype(ec)::value;
+      before(ec);  // work placed ahead of element e (tile loads, softmax parts)
+      if constexpr (e + kAhead < kN) issue(e + kAhead);
+      constexpr int i = index(e);
+      if constexpr (is_s(e)) {
         f32x16& sb = (i & 1) ? s1 : s0;
         sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[i % kRing], qf[i >> 1], sb, 0, 0, 0);
         if constexpr (kSplitQ)
@@ -562,15 +581,23 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
         acc[i & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vr[i % kRing]), p[i >> 3],
                                                             acc[i & 7], 0, 0, 0);
       }
-    }
+    });
   };
 
-  // Softmax of one tile's scores into pb. The running max moves only when
-  // the tile's max exceeds it by more than 2^8; returns the factor O must be
-  // rescaled by (1 when the max did not move).
-  auto softmax = [&](f32x16& s0, f32x16& s1, bf16x8* pb, float& alpha) __attribute__((always_inline)) {
-    // reductions as balanced trees: short dependency chains interleave
-    // with the matrix-core stream without stalling it
+  // Softmax of one tile's scores into pb, in three parts that the step
+  // spreads over its stream: the max (the running max moves only when the
+  // tile's max exceeds it by more than 2^8; alpha is the factor O must be
+  // rescaled by, 1 when the max did not move), the probabilities of score
+  // registers i0 .. i1-1, and the sum. Reductions are balanced trees: short
+  // dependency chains interleave with the matrix-core stream without
+  // stalling it.
+  struct SoftmaxPart {
+    float m_use;
+    bool rescale;
+    float q16[16];
+  };
+  auto softmax_max = [&](const f32x16& s0, const f32x16& s1, SoftmaxPart& sp, float& alpha)
+                         __attribute__((always_inline)) {
     float t16[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) t16[i] = max_f(s0[i], s1[i]);
@@ -580,27 +607,30 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
       for (int i = 0; i < w; ++i) t16[i] = max_f(t16[i], t16[i + w]);
     const float mx = pair_max(t16[0]) * kScoreScale;
     const float m_new = max_f(m_i, mx);
-    const bool rescale = __any(m_new > m_i + kRescaleSlack);
-    const float m_use = rescale ? m_new : m_i;
-    alpha = fast_exp2(m_i - m_use);
-    // step tt of P^T covers keys 16tt .. +15; its key slot (lane/32)*8 + j
-    // is register 8*(tt%2) + j of block tt/2
-    float q16[16];
+    sp.rescale = __any(m_new > m_i + kRescaleSlack);
+    sp.m_use = sp.rescale ? m_new : m_i;
+    alpha = fast_exp2(m_i - sp.m_use);
+  };
+  // step tt of P^T covers keys 16tt .. +15; its key slot (lane/32)*8 + j
+  // is register 8*(tt%2) + j of block tt/2
+  auto softmax_exp = [&](const f32x16& s0, const f32x16& s1, bf16x8* pb, SoftmaxPart& sp, int i0, int i1)
+                         __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p0 = fast_exp2(fmaf(s0[i], kScoreScale, -m_use));
-      const float p1 = fast_exp2(fmaf(s1[i], kScoreScale, -m_use));
-      q16[i] = p0 + p1;
+    for (int i = i0; i < i1; ++i) {
+      const float p0 = fast_exp2(fmaf(s0[i], kScoreScale, -sp.m_use));
+      const float p1 = fast_exp2(fmaf(s1[i], kScoreScale, -sp.m_use));
+      sp.q16[i] = p0 + p1;
       pb[i >> 3][i & 7] = (__bf16)p0;
       pb[2 + (i >> 3)][i & 7] = (__bf16)p1;
     }
+  };
+  auto softmax_sum = [&](SoftmaxPart& sp, float alpha) __attribute__((always_inline)) {
 #pragma unroll
     for (int w = 8; w >= 1; w >>= 1)
 #pragma unroll
-      for (int i = 0; i < w; ++i) q16[i] += q16[i + w];
-    l_i = l_i * alpha + q16[0];   // per-lane partial; the lane pair is summed at the end
-    m_i = m_use;
-    return rescale;
+      for (int i = 0; i < w; ++i) sp.q16[i] += sp.q16[i + w];
+    l_i = l_i * alpha + sp.q16[0];   // per-lane partial; the lane pair is summed at the end
+    m_i = sp.m_use;
   };
   // O *= alpha in place in the accumulation registers (read, multiply,
   // write back per element), so O never has to move to VGPRs.
@@ -633,7 +663,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   bf16x8 pA[4], pB[4];        // probabilities of even / odd tiles
   wait_loads();
   __syncthreads();
-  mma_stream(ModeS{}, k_lds0, v_lds0, sA0, sA1, pA, [](int) {});
+  mma_stream(ModeS{}, k_lds0, v_lds0, sA0, sA1, pA, [](auto) {});
   issue_order<kStreamS, 0, kSplitQ>();
   if (need_mask(t_lo)) mask_s(t_lo, sA0, sA1);
 
@@ -666,10 +696,39 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
     // rescale would only multiply zeros (the running sum is rescaled inside
     // the softmax).
     if (rescale_pending && j > 1) rescale_o(alpha_pending);
-    mma_stream(mode, kn, vp, sn0, sn1, pp, [&](int e) __attribute__((always_inline)) {
-        if (e % kLoadSpacing == 0 && e < 4 * kLoadSpacing && wave == e / kLoadSpacing) load_tiles();
+    // The softmax of S(t) runs beside the stream. With split queries (twice
+    // the S MFMAs) its max goes beside elements 0-7, the probabilities of
+    // score registers 0-3 and 4-7 beside 8-15 and 16-23, the rest and the
+    // sum beside the long last block; each part is pinned where it is placed
+    // (ahead of the next load branch), so the compiler cannot sink it into
+    // the next block. The plain kernel keeps the whole softmax in the last
+    // block, which measured faster there.
+    SoftmaxPart sp;
+    mma_stream(mode, kn, vp, sn0, sn1, pp, [&](auto ec) __attribute__((always_inline)) {
+        constexpr int e = decltype(ec)::value;
+        if constexpr (!kSplitQ) {
+        } else if constexpr (e == kLoadSpacing) {
+          softmax_max(sc0, sc1, sp, alpha_pending);
+          asm volatile("" : "+v"(sp.m_use), "+v"(alpha_pending));
+          issue_order_block<kMode, 0, kSoftmaxValuPerMfmaEarly, kSplitQ>();
+        } else if constexpr (e == 2 * kLoadSpacing || e == 3 * kLoadSpacing) {
+          constexpr int i0 = e == 2 * kLoadSpacing ? 0 : 4;
+          softmax_exp(sc0, sc1, pn, sp, i0, i0 + 4);
+          asm volatile("" : "+v"(pn[0]), "+v"(pn[2]), "+v"(sp.q16[i0]), "+v"(sp.q16[i0 + 1]),
+                       "+v"(sp.q16[i0 + 2]), "+v"(sp.q16[i0 + 3]));
+          issue_order_block<kMode, e - kLoadSpacing, kSoftmaxValuPerMfmaEarly, kSplitQ>();
+        }
+        if constexpr (e % kLoadSpacing == 0 && e < 4 * kLoadSpacing) {
+          if (wave == e / kLoadSpacing) load_tiles();
+        }
     });
-    rescale_pending = softmax(sc0, sc1, pn, alpha_pending);
+    if constexpr (!kSplitQ) {
+      softmax_max(sc0, sc1, sp, alpha_pending);
+      softmax_exp(sc0, sc1, pn, sp, 0, 8);
+    }
+    softmax_exp(sc0, sc1, pn, sp, 8, 16);
+    softmax_sum(sp, alpha_pending);
+    rescale_pending = sp.rescale;
     issue_order<kMode, kSoftmaxValuPerMfma, kSplitQ>();
     // The softmax's results are used here, ahead of the mask branch: nothing
     // below needs them before the next step, and without this use the
@@ -695,10 +754,10 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   __syncthreads();
   if (rescale_pending && nt > 1) rescale_o(alpha_pending);
   if ((nt - 1) & 1) {
-    mma_stream(ModePv{}, k_lds0, v_lds1, sA0, sA1, pB, [](int) {});
+    mma_stream(ModePv{}, k_lds0, v_lds1, sA0, sA1, pB, [](auto) {});
     issue_order<kStreamPv, 0, kSplitQ>();
   } else {
-    mma_stream(ModePv{}, k_lds0, v_lds0, sA0, sA1, pA, [](int) {});
+    mma_stream(ModePv{}, k_lds0, v_lds0, sA0, sA1, pA, [](auto) {});
     issue_order<kStreamPv, 0, kSplitQ>();
   }
   l_i = pair_sum(l_i);
