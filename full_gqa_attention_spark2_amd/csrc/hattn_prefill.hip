@@ -51,6 +51,7 @@ constexpr float kScoreScale = kLog2e / 16.0f;    // 1/sqrt(256), in log2 units
 constexpr float kRescaleSlack = 8.0f;            // log2 units
 
 typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4q __attribute__((ext_vector_type(4)));  // a buffer descriptor in scalar registers
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ s16x4 lds_read_tr(const char* p) {
@@ -299,9 +300,10 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
     load_tile(kPaged ? page_rsrc(a.kc, t) : krs, false, t, slot);
   };
 
-  // The first K tiles: requested right after the query loads below, so they
-  // are in flight during the query RoPE. (V of the first tile is loaded by
-  // the first step, ahead of its P.V in the second.)
+  // The first K tiles, in flight during the query RoPE. (The fast query
+  // path below requests the second one only once its queries, staged in
+  // that tile's slot, have been read; V of the first tile is loaded by the
+  // first step, ahead of its P.V in the second.)
   auto load_first_tiles = [&]() __attribute__((always_inline)) {
     load_k(t_lo, k_lds0);
     if (nt > 1) load_k(t_lo + 1, k_lds1);
@@ -317,6 +319,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   const uint16_t gate_bits = a.gate[orow];
   bf16x8 qf[16];
   bf16x8 qlo[kSplitQ ? 16 : 1];
+  const bool late_second_tile = a.r == 64 || a.r == 256;  // the fast query path below
   {
     const int qr = qvalid ? qrow : len - 1;
     const uint16_t* qp = a.q + (tok0 + qr) * (size_t)a.q_stride + (size_t)h * kHeadDim;
@@ -349,20 +352,62 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
           load_lds16(trs, src, 0, v_lds1 + (wave * NP + u) * 1024);
         }
       }
-      asm volatile("" ::: "memory");  // issue order: table rows, then queries, then first tiles
-      uint4 raw[16];
+      // The wave's 32 query rows (512 B of its head each) come the same way
+      // into 16 KiB of the slots k_lds1 and v_lds0, which the second K tile
+      // and the first V tile fill only after the queries have been read:
+      // instruction u fills rows 2u, 2u + 1 from whole lines, instead of 16
+      // loads per lane that each touch 32 rows. Row i keeps its 16-byte
+      // chunk c at position c ^ (i & 31), so the 16 lanes of a fragment read
+      // hit 16 different bank groups. Rows past the end repeat row nq - 1.
+      // These copies are issued from inline asm (waited for below by count):
+      // through the builtin, the compiler could not tell which slot the
+      // selected pointer writes and waited for the K tile's copies too
+      // before reading the queries.
+      const char* qst = (wave < 2 ? k_lds1 : v_lds0) + (wave & 1) * 16384;
+      {
+        const uint16_t* qbase = a.q + (tok0 + q0) * (size_t)a.q_stride + (size_t)h * kHeadDim;
+        const uint64_t qa = (uint64_t)(uintptr_t)qbase;
+        const uint32_t qbytes = (uint32_t)(nq - 1) * (uint32_t)a.q_stride * 2u + 512u;
+        const int d0 = __builtin_amdgcn_readfirstlane((int)(uint32_t)qa);
+        const int d1 = __builtin_amdgcn_readfirstlane((int)((qa >> 32) & 0xffff));
+        const int d2 = __builtin_amdgcn_readfirstlane((int)qbytes);
+        const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_u32(qst));
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) raw[ks] = *(const uint4*)(qp + ks * 16 + (lane >> 5) * 8);
-      asm volatile("" ::: "memory");
-      load_first_tiles();
-      // This wave's table rows have landed once at most the 16 query loads
-      // and the first tiles' 8 or 16 loads are outstanding; after the
-      // barrier, every wave's have. (A bare s_barrier: __syncthreads would
-      // also wait for the queries and the tiles.)
-      if (nt > 1) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+        for (int u = 0; u < 16; ++u) {
+          const int i = 2 * u + (lane >> 5);
+          const uint32_t c = (uint32_t)((lane & 31) ^ (i & 31));
+          const uint32_t voff = (uint32_t)min(i, nq - 1) * (uint32_t)a.q_stride * 2u + 16u * c;
+          asm volatile(
+              "s_mov_b32 m0, %0\n\t"
+              "s_nop 0\n\t"
+              "buffer_load_dwordx4 %1, %2, 0 offen lds"
+              :
+              : "s"(m0 + 1024u * (uint32_t)u), "v"(voff), "s"(i32x4q{d0, d1, d2, 0x00020000})
+              : "memory", "m0");
+        }
+      }
+      asm volatile("" ::: "memory");  // issue order: table rows, queries, then the first K tile
+      load_k(t_lo, k_lds0);
+      // This wave's table rows and queries have landed once at most the
+      // first tile's 8 loads are outstanding; after the barrier, every
+      // wave's have. (A bare s_barrier: __syncthreads would also wait for
+      // the tile.)
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
+      // The query reads are asm as well: the compiler, not seeing the copies
+      // above, would otherwise still wait for the K tile's copy before them.
+      uint4 raw[16];
+      {
+        const int i = lane & 31;
+        const uint32_t qrow = lds_u32(qst) + (uint32_t)i * 512u;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+          const uint32_t ad = qrow + 16u * (uint32_t)((2 * ks + (lane >> 5)) ^ i);
+          asm volatile("ds_read_b128 %0, %1" : "=v"(raw[ks]) : "v"(ad) : "memory");
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      }
       uint4 cs[NP][4];  // (cos, sin) of table entries 16p + 8(lane/32) + 0..7
       {
         const int i = qr - q0;
@@ -412,6 +457,11 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
         qf[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
         if constexpr (kSplitQ) qlo[ks] = bf16x8{};
       }
+      // every wave has read its queries: the second K tile may replace them
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (nt > 1) load_k(t_lo + 1, k_lds1);
     };
     // Any other r (a multiple of 16): fragment by fragment, partners and
     // table entries loaded per fragment.
@@ -661,8 +711,13 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
   float alpha_pending = 1.0f;
   f32x16 sA0, sA1, sB0, sB1;  // scores of even / odd tiles
   bf16x8 pA[4], pB[4];        // probabilities of even / odd tiles
-  wait_loads();
-  __syncthreads();
+  // The first K tile has landed once at most the second one's 8 loads are
+  // outstanding: the fast query path requests that tile only at its end
+  // (the other path requests both up front).
+  if (late_second_tile && nt > 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else wait_loads();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   mma_stream(ModeS{}, k_lds0, v_lds0, sA0, sA1, pA, [](auto) {});
   issue_order<kStreamS, 0, kSplitQ>();
   if (need_mask(t_lo)) mask_s(t_lo, sA0, sA1);
