@@ -249,6 +249,8 @@ size_t decode_workspace_bytes(const hattn_layer_desc* desc, const hattn_kv_cache
 // start_pos[b] + 0 .. len[b] - 1.
 // Token rows of q, k/v and gate are q_stride, kv_stride and gate_stride
 // elements apart (dense: Hq * 256, Hkv * 256, Hq).
+constexpr long long kMaxQStride = 1LL << 24;  // 65,536 query heads of 256 channels
+
 int prefill_packed(const hattn_layer_desc* desc, const void* q, const void* k, const void* v,
                    const void* gate, int32_t batch, const int* tok0, const int* len, long long total,
                    const int32_t* start_pos, const hattn_kv_cache* cache, void* out, void* workspace,
@@ -275,6 +277,9 @@ int prefill_packed(const hattn_layer_desc* desc, const void* q, const void* k, c
   // (A paged cache is addressed per page.)
   const long long key_rows = ring ? (long long)desc->window - 1 + max_len : (long long)cache->capacity;
   if (cache->kind != HATTN_KV_PAGED && key_rows > kMaxPrefillKeyRows) return HATTN_ERR_UNSUPPORTED;
+  // A query block's 32 rows are read with 32-bit byte offsets from its first
+  // row (q_stride elements apart).
+  if (q_stride > kMaxQStride) return HATTN_ERR_UNSUPPORTED;
   // one-dimensional grids: (query blocks x sequences x KV heads) workgroups
   if ((long long)((max_len + kPrefillBlockQ - 1) / kPrefillBlockQ) * batch * desc->num_kv_heads > INT32_MAX)
     return HATTN_ERR_UNSUPPORTED;

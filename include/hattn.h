@@ -157,7 +157,8 @@ size_t hattn_prefill_workspace_size(const hattn_layer_desc* desc,
  * 128; the key rows of one (sequence, KV head) -- a linear cache's
  * capacity, or window - 1 + S for a ring; paged caches are addressed page
  * by page and exempt -- at most 2^23; ceil(S / 32) * B * num_kv_heads
- * below 2^31.
+ * below 2^31; num_q_heads at most 65,536 (a query block's rows are read
+ * with 32-bit byte offsets).
  * Numerics: keys are rotated in fp64 and cached as bf16 (one rounding);
  * the scores take the rotated queries as bf16 on full layers and as a bf16
  * high part plus a bf16 low part (~16 significant bits) on sliding layers;

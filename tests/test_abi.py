@@ -100,6 +100,8 @@ def test_prefill_rejects_bad_arguments(L):
     big = hb.KvCacheC(FAKE, FAKE, hb.KV_LINEAR, 1, (1 << 23) + 1)
     cases.append((fu, big, {}, -3))                                                    # 32-bit row offsets
     cases.append((sl, ring, {"S": (1 << 23) - 510}, -3))                                 # 511 + S rows
+    d = hb.layer_desc("full"); d.num_q_heads = 65540; d.num_kv_heads = 16385
+    cases.append((d, lin, {}, -3))                                                     # 32-bit query row offsets
     for desc, cache, kw, want in cases:
         got = _prefill(L, desc, cache, **kw)
         assert got == want, (desc.layer_type, kw, got, want)
