@@ -401,12 +401,25 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillAttnArgs a)
       {
         const int i = lane & 31;
         const uint32_t qrow = lds_u32(qst) + (uint32_t)i * 512u;
+        i32x4q rv[16];
 #pragma unroll
         for (int ks = 0; ks < 16; ++ks) {
           const uint32_t ad = qrow + 16u * (uint32_t)((2 * ks + (lane >> 5)) ^ i);
-          asm volatile("ds_read_b128 %0, %1" : "=v"(raw[ks]) : "v"(ad) : "memory");
+          asm volatile("ds_read_b128 %0, %1" : "=v"(rv[ks]) : "v"(ad) : "memory");
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        // The wait names the 16 results as operands, so no use of them can
+        // be scheduled ahead of it (the hardware does not hold a VALU read
+        // of a register an LDS read is still filling).
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(rv[0]), "+v"(rv[1]), "+v"(rv[2]), "+v"(rv[3]), "+v"(rv[4]), "+v"(rv[5]), "+v"(rv[6]),
+                       "+v"(rv[7])
+                     :
+                     : "memory");
+        asm volatile(""
+                     : "+v"(rv[8]), "+v"(rv[9]), "+v"(rv[10]), "+v"(rv[11]), "+v"(rv[12]), "+v"(rv[13]),
+                       "+v"(rv[14]), "+v"(rv[15]));
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) raw[ks] = __builtin_bit_cast(uint4, rv[ks]);
       }
       uint4 cs[NP][4];  // (cos, sin) of table entries 16p + 8(lane/32) + 0..7
       {
