@@ -164,6 +164,15 @@ int check_weights(const hattn_layer_desc* d, const hattn_block_weights* w) {
   return HATTN_OK;
 }
 
+// Row stride of the fused q/k/v/g projection's output: its (Hq + 2 Hkv) * 256
+// + Hq columns rounded up to a multiple of 8, so every row (and every q, k,
+// v slice in it) starts 16-byte aligned, as the kernels' 16-byte loads of
+// those rows require.
+long long fused_row_stride(int Hq, int Hkv) {
+  const long long n1 = (long long)(Hq + 2 * Hkv) * 256 + Hq;
+  return (n1 + 7) / 8 * 8;
+}
+
 // Workspace of one block call over T tokens: h [T][hidden], the fused
 // projection [T][N1], the core's output [T][Hq*256], the out_proj result
 // [T][hidden], the GEMM workspace, then the core's own workspace.
@@ -172,7 +181,7 @@ struct BlockLayout {
 };
 BlockLayout block_layout(const hattn_layer_desc* d, const hattn_block_weights* w, long long T, size_t core) {
   BlockLayout L{};
-  const long long n1 = (long long)(d->num_q_heads + 2 * d->num_kv_heads) * 256 + d->num_q_heads;
+  const long long n1 = fused_row_stride(d->num_q_heads, d->num_kv_heads);
   L.h = 0;
   L.qkvg = L.h + align256((size_t)T * w->hidden * 2);
   L.attn = L.qkvg + align256((size_t)T * n1 * 2);
@@ -189,7 +198,8 @@ template <class Core>
 int block_run(const hattn_layer_desc* desc, const hattn_block_weights* w, const void* x, long long T,
               void* out, char* ws, const BlockLayout& L, hipStream_t s, Core core) {
   const int Hq = desc->num_q_heads, Hkv = desc->num_kv_heads, H = w->hidden;
-  const long long n1 = (long long)(Hq + 2 * Hkv) * 256 + Hq;
+  const long long n1 = (long long)(Hq + 2 * Hkv) * 256 + Hq;  // fused projection outputs
+  const long long ld1 = fused_row_stride(Hq, Hkv);             // their row stride
   uint16_t* h = (uint16_t*)(ws + L.h);
   uint16_t* qkvg = (uint16_t*)(ws + L.qkvg);
   uint16_t* attn = (uint16_t*)(ws + L.attn);
@@ -202,10 +212,10 @@ int block_run(const hattn_layer_desc* desc, const hattn_block_weights* w, const 
   na.H = H;
   na.eps = w->rms_eps;
   if (launch_rms_norm(na, s) != hipSuccess) return HATTN_ERR_LAUNCH;
-  int st = gemm(w->qkvg_weight, (int)n1, H, h, (int)T, H, qkvg, n1, ws + L.gemm, s);
+  int st = gemm(w->qkvg_weight, (int)n1, H, h, (int)T, H, qkvg, ld1, ws + L.gemm, s);
   if (st != HATTN_OK) return st;
   st = core(qkvg, qkvg + (size_t)Hq * 256, qkvg + (size_t)(Hq + Hkv) * 256, qkvg + (size_t)(Hq + 2 * Hkv) * 256,
-            n1, attn);
+            ld1, attn);
   if (st != HATTN_OK) return st;
   bool fused = false;
   st = gemm(w->o_weight, H, Hq * 256, attn, (int)T, (long long)Hq * 256, y, H, ws + L.gemm, s, (const float*)x,

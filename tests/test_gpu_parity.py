@@ -685,6 +685,7 @@ def _block(hidden, Hq, Hkv, seed):
 @pytest.mark.parametrize("layer,hidden,Hq,Hkv,kind,cap", [
     ("full", 2560, 16, 4, "linear", 2048),     # the 4B shape
     ("sliding", 2048, 8, 2, "ring", 512),      # the 1.7B shape
+    ("sliding", 1024, 4, 1, "ring", 512),      # 1540 fused outputs: rows padded to 1544 for alignment
 ])
 def test_block_prefill_and_decode(layer, hidden, Hq, Hkv, kind, cap):
     # RMSNorm -> fused q/k/v/g projection -> core -> out_proj -> + residual,
